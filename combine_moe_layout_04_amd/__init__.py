@@ -1,0 +1,20 @@
+"""MoE token layout, dispatch and combine for MI355X (gfx950).
+
+The hot path is hand-written HIP in ``csrc/`` behind the C ABI of
+``include/moe_layout.h``; this package is its thin Python binding.
+"""
+from .api import (  # noqa: F401
+    FIELDS,
+    Handle,
+    MoeError,
+    moe_bench_copy,
+    moe_combine,
+    moe_combine_bwd,
+    moe_dispatch,
+    moe_dispatch_bwd,
+    moe_layout,
+    moe_workspace_size,
+)
+from . import autograd  # noqa: F401
+
+__version__ = "0.1.0"

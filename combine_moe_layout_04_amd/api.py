@@ -1,0 +1,277 @@
+"""Python binding of the C ABI in include/moe_layout.h, with the same names.
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity), outputs are allocated with torch when the caller passes none,
+and the call goes to the HIP library on torch's current stream.  Every step
+of the path runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import MoeTuning, lib
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_I32, MOE_I64 = 0, 1
+STATUS_BAD_EXPERT, STATUS_BAD_POSITION = 1, 2
+
+FIELDS = {  # name -> (id, dtype, shape as a function of (T,K,E,P))
+    "num_tokens_per_expert": (0, torch.int32, lambda T, K, E, P: (E,)),
+    "num_tokens_per_rank": (1, torch.int32, lambda T, K, E, P: (P,)),
+    "is_token_in_rank": (2, torch.uint8, lambda T, K, E, P: (T, P)),
+    "expert_offset": (3, torch.int32, lambda T, K, E, P: (E + 1,)),
+    "rank_offset": (4, torch.int32, lambda T, K, E, P: (P + 1,)),
+    "send_offset": (5, torch.int32, lambda T, K, E, P: (P + 1,)),
+    "token_slot": (6, torch.int32, lambda T, K, E, P: (T, P)),
+    "recv_pos": (7, torch.int32, lambda T, K, E, P: (T, K)),
+    "recv_token": (8, torch.int32, lambda T, K, E, P: (T * K,)),
+    "recv_k": (9, torch.int32, lambda T, K, E, P: (T * K,)),
+    "status": (10, torch.int32, lambda T, K, E, P: (1,)),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = lib().moe_strerror(code).decode()
+        super().__init__(f"{where}: {msg} (status {code})")
+        self.code = code
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise MoeError(rc, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"rows must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, device, shape=None, dtype=None):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def moe_workspace_size(T: int, K: int, E: int, P: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(T, K, E, P, ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+class Handle:
+    """Opaque layout handle plus the device workspace its arrays live in."""
+
+    def __init__(self, chunks_per_lane: int = 0, nontemporal: int = 1, waves_per_block: int = 0):
+        tun = MoeTuning(chunks_per_lane, nontemporal, waves_per_block)
+        h = ctypes.c_void_p()
+        _check(lib().moe_handle_create(ctypes.byref(h), ctypes.byref(tun)), "moe_handle_create")
+        self._h = h
+        self.workspace: Optional[torch.Tensor] = None
+        self.T = self.K = self.E = self.P = None
+        self.device = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                lib().moe_handle_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    @property
+    def ptr(self) -> ctypes.c_void_p:
+        return self._h
+
+    def field(self, name: str) -> torch.Tensor:
+        """A view (no copy, no sync) of one handle field inside the workspace."""
+        fid, dt, shape = FIELDS[name]
+        p = ctypes.c_void_p()
+        n = ctypes.c_size_t()
+        _check(lib().moe_handle_field(self._h, fid, ctypes.byref(p), ctypes.byref(n)), "moe_handle_field")
+        off = (p.value or 0) - self.workspace.data_ptr()
+        raw = self.workspace[off:off + n.value]
+        return raw.view(dt).reshape(shape(self.T, self.K, self.E, self.P))
+
+    def check(self) -> int:
+        """Synchronises the current stream and returns the device status bits."""
+        v = ctypes.c_int(0)
+        _check(lib().moe_handle_check(self._h, _stream(self.device), ctypes.byref(v)), "moe_handle_check")
+        return v.value
+
+
+def moe_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
+               handle: Optional[Handle] = None, workspace: Optional[torch.Tensor] = None) -> Handle:
+    """Layout of one routing decision; returns the handle (see moe_layout.h)."""
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, K]")
+    dev = topk_idx.device
+    _need(topk_idx, "topk_idx", dev)
+    if topk_idx.dtype == torch.int32:
+        itype = MOE_I32
+    elif topk_idx.dtype == torch.int64:
+        itype = MOE_I64
+    else:
+        raise TypeError("topk_idx must be int32 or int64")
+    T, K = topk_idx.shape
+    E, P = int(num_experts), int(num_partitions)
+    need = moe_workspace_size(T, K, E, P)
+    h = handle if handle is not None else Handle()
+    if workspace is None:
+        ws = h.workspace
+        if ws is None or ws.numel() < need or ws.device != dev:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", dev, dtype=torch.uint8)
+        ws = workspace
+    _check(lib().moe_layout(h.ptr, _ptr(topk_idx), itype, T, K, E, P, _ptr(ws), ws.numel(),
+                            _stream(dev)), "moe_layout")
+    h.workspace, h.T, h.K, h.E, h.P, h.device = ws, T, K, E, P, dev
+    return h
+
+
+def moe_dispatch(handle: Handle, x: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                 scale_rows: bool = False, recv: Optional[torch.Tensor] = None,
+                 recv_scores=None):
+    """recv[recv_pos[t,k]] = x[t] (scaled by w[t,k] if scale_rows).
+
+    recv_scores: None (not produced), True (allocate) or a float32 [R] tensor.
+    Returns (recv, recv_scores or None)."""
+    h = handle
+    dev = h.device
+    T, K = h.T, h.K
+    _need(x, "x", dev)
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError(f"x must be [{T}, H]")
+    H = x.shape[1]
+    dt = _dtype_code(x)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", dev, (T, K), torch.float32)
+    if recv is None:
+        recv = torch.empty((T * K, H), dtype=x.dtype, device=dev)
+    _need(recv, "recv", dev, (T * K, H), x.dtype)
+    if recv_scores is True:
+        recv_scores = torch.empty(T * K, dtype=torch.float32, device=dev)
+    elif recv_scores is False:
+        recv_scores = None
+    if recv_scores is not None:
+        _need(recv_scores, "recv_scores", dev, (T * K,), torch.float32)
+    _check(lib().moe_dispatch(h.ptr, _ptr(x), dt, H, _ptr(topk_weights), int(bool(scale_rows)),
+                              _ptr(recv), _ptr(recv_scores), _stream(dev)), "moe_dispatch")
+    return recv, recv_scores
+
+
+def moe_combine(handle: Handle, y: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = sum_k [w[t,k] *] y[recv_pos[t,k]] (float32, k order)."""
+    h = handle
+    dev = h.device
+    T, K = h.T, h.K
+    _need(y, "y", dev)
+    if y.dim() != 2 or y.shape[0] != T * K:
+        raise ValueError(f"y must be [{T * K}, H]")
+    H = y.shape[1]
+    dt = _dtype_code(y)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", dev, (T, K), torch.float32)
+    if out is None:
+        out = torch.empty((T, H), dtype=y.dtype, device=dev)
+    _need(out, "out", dev, (T, H), y.dtype)
+    _check(lib().moe_combine(h.ptr, _ptr(y), dt, H, _ptr(topk_weights), _ptr(out), _stream(dev)),
+           "moe_combine")
+    return out
+
+
+def moe_combine_bwd(handle: Handle, grad_out: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                    y: Optional[torch.Tensor] = None, grad_y: Optional[torch.Tensor] = None,
+                    grad_w=None):
+    """grad_y[recv_pos[t,k]] = [w[t,k] *] grad_out[t]; grad_w[t,k] = <grad_out[t], y[row]>.
+
+    grad_w: None (not produced), True (allocate) or a float32 [T,K] tensor.
+    Returns (grad_y, grad_w or None)."""
+    h = handle
+    dev = h.device
+    T, K = h.T, h.K
+    _need(grad_out, "grad_out", dev)
+    if grad_out.dim() != 2 or grad_out.shape[0] != T:
+        raise ValueError(f"grad_out must be [{T}, H]")
+    H = grad_out.shape[1]
+    dt = _dtype_code(grad_out)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", dev, (T, K), torch.float32)
+    if y is not None:
+        _need(y, "y", dev, (T * K, H), grad_out.dtype)
+    if grad_y is None:
+        grad_y = torch.empty((T * K, H), dtype=grad_out.dtype, device=dev)
+    _need(grad_y, "grad_y", dev, (T * K, H), grad_out.dtype)
+    if grad_w is True:
+        grad_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    elif grad_w is False:
+        grad_w = None
+    if grad_w is not None:
+        _need(grad_w, "grad_w", dev, (T, K), torch.float32)
+    _check(lib().moe_combine_bwd(h.ptr, _ptr(grad_out), dt, H, _ptr(topk_weights), _ptr(y),
+                                 _ptr(grad_y), _ptr(grad_w), _stream(dev)), "moe_combine_bwd")
+    return grad_y, grad_w
+
+
+def moe_dispatch_bwd(handle: Handle, grad_recv: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                     x: Optional[torch.Tensor] = None, grad_x: Optional[torch.Tensor] = None,
+                     grad_s=None):
+    """grad_x[t] = sum_k [w[t,k] *] grad_recv[recv_pos[t,k]]; grad_s[t,k] = <grad_recv[row], x[t]>.
+
+    Pass topk_weights iff the forward dispatch scaled its rows.
+    grad_s: None, True (allocate) or a float32 [T,K] tensor.
+    Returns (grad_x, grad_s or None)."""
+    h = handle
+    dev = h.device
+    T, K = h.T, h.K
+    _need(grad_recv, "grad_recv", dev)
+    if grad_recv.dim() != 2 or grad_recv.shape[0] != T * K:
+        raise ValueError(f"grad_recv must be [{T * K}, H]")
+    H = grad_recv.shape[1]
+    dt = _dtype_code(grad_recv)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", dev, (T, K), torch.float32)
+    if x is not None:
+        _need(x, "x", dev, (T, H), grad_recv.dtype)
+    if grad_x is None:
+        grad_x = torch.empty((T, H), dtype=grad_recv.dtype, device=dev)
+    _need(grad_x, "grad_x", dev, (T, H), grad_recv.dtype)
+    if grad_s is True:
+        grad_s = torch.empty((T, K), dtype=torch.float32, device=dev)
+    elif grad_s is False:
+        grad_s = None
+    if grad_s is not None:
+        _need(grad_s, "grad_s", dev, (T, K), torch.float32)
+    _check(lib().moe_dispatch_bwd(h.ptr, _ptr(grad_recv), dt, H, _ptr(topk_weights), _ptr(x),
+                                  _ptr(grad_x), _ptr(grad_s), _stream(dev)), "moe_dispatch_bwd")
+    return grad_x, grad_s
+
+
+def moe_bench_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """Plain device copy (calibration kernel for HBM traffic counters)."""
+    if dst.numel() * dst.element_size() != src.numel() * src.element_size():
+        raise ValueError("size mismatch")
+    _check(lib().moe_bench_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
+                                _stream(src.device)), "moe_bench_copy")

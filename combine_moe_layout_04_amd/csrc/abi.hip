@@ -1,0 +1,372 @@
+// C ABI of libmoe_layout.so: host-side validation, the workspace plan, the
+// opaque handle and stream-ordered launches.  Every argument error is caught
+// here, before any HIP call, so a rejected call launches nothing.
+#include <new>
+
+#include "internal.h"
+#include "../../include/moe_layout.h"
+
+struct moe_handle_s {
+  static constexpr uint32_t kMagic = 0x4D4F454Cu;  // "MOEL"
+  uint32_t magic = kMagic;
+  bool has_layout = false;
+  int64_t T = 0;
+  int K = 0, E = 0, P = 0;
+  char* ws = nullptr;
+  moe::WsLayout plan{};
+  moe::Tuning tune{};
+};
+
+namespace moe {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+WsLayout plan_workspace(int64_t T, int K, int E, int P) {
+  WsLayout w{};
+  // layout tiles: at most ~128 workgroups, whole wavefronts of tokens each,
+  // at most 4096 tokens per tile (the count kernel keeps their masks in LDS)
+  int64_t tile = 64 * ((T + 64 * 128 - 1) / (64 * 128));
+  if (tile < 64) tile = 64;
+  if (tile > 4096) tile = 4096;
+  int64_t nblk = (T + tile - 1) / tile;
+  if (nblk < 1) nblk = 1;
+  w.tile = (int)tile;
+  w.nblk = (int)nblk;
+  const int64_t R = T * K;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + (bytes ? bytes : 1), 256);
+    return at;
+  };
+  w.status = take(4);
+  w.num_tokens_per_expert = take((size_t)E * 4);
+  w.num_tokens_per_rank = take((size_t)P * 4);
+  w.expert_offset = take((size_t)(E + 1) * 4);
+  w.rank_offset = take((size_t)(P + 1) * 4);
+  w.send_offset = take((size_t)(P + 1) * 4);
+  w.is_token_in_rank = take((size_t)T * P);
+  w.token_slot = take((size_t)T * P * 4);
+  w.recv_pos = take((size_t)R * 4);
+  w.recv_token = take((size_t)R * 4);
+  w.recv_k = take((size_t)R * 4);
+  w.tok_mask = take((size_t)T * 8);
+  w.ehist = take((size_t)(E + 1) * nblk * 4);
+  w.rhist = take((size_t)P * nblk * 4);
+  w.total = o;
+  return w;
+}
+
+}  // namespace moe
+
+namespace {
+
+bool valid_handle(const moe_handle_s* h) { return h && h->magic == moe_handle_s::kMagic; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 0; }
+
+int check_shape(int64_t T, int K, int E, int P) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (K < 1 || E < 1 || P < 1) return MOE_ERR_SHAPE;
+  if (K > MOE_MAX_K || E > MOE_MAX_E || P > MOE_MAX_P) return MOE_ERR_UNSUPPORTED;
+  if (E % P != 0 || K > E) return MOE_ERR_SHAPE;
+  if (T * (int64_t)K >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Shared checks of the four row calls.  Returns MOE_OK and NV (16-byte chunks
+// per row), or an error.
+int check_rows(const moe_handle_s* h, int dtype, int64_t H, int* NV) {
+  if (!valid_handle(h)) return MOE_ERR_INVALID_ARG;
+  if (!h->has_layout) return MOE_ERR_HANDLE;
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return MOE_ERR_UNSUPPORTED;
+  if (H < 1 || (H * eb) % 16 != 0) return MOE_ERR_SHAPE;
+  const int64_t nv = H * eb / 16;
+  if (nv >= (int64_t(1) << 31) || nv * h->T * h->K >= (int64_t(1) << 62)) return MOE_ERR_UNSUPPORTED;
+  *NV = (int)nv;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+template <typename T>
+T* ws_ptr(const moe_handle_s* h, size_t off) {
+  return reinterpret_cast<T*>(h->ws + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(int64_t T, int K, int E, int P, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const int st = check_shape(T, K, E, P);
+  if (st != MOE_OK) return st;
+  *bytes = moe::plan_workspace(T, K, E, P).total;
+  return MOE_OK;
+}
+
+int moe_handle_create(moe_handle_t* out, const moe_tuning* tuning) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  moe::Tuning t{4, 1, 4};  // defaults: 4 chunks/lane (scatter), receive-row NT stores, 4 waves/WG
+  if (tuning) {
+    const int c = tuning->chunks_per_lane, n = tuning->nontemporal, w = tuning->waves_per_block;
+    if (!(c == 0 || c == 1 || c == 2 || c == 4)) return MOE_ERR_INVALID_ARG;
+    if (n < 0 || n > 2) return MOE_ERR_INVALID_ARG;
+    if (!(w == 0 || w == 1 || w == 2 || w == 4 || w == 8)) return MOE_ERR_INVALID_ARG;
+    if (c) t.chunks_per_lane = c;
+    t.nontemporal = n;
+    if (w) t.waves_per_block = w;
+  }
+  moe_handle_s* h = new (std::nothrow) moe_handle_s();
+  if (!h) return MOE_ERR_INVALID_ARG;
+  h->tune = t;
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_handle_destroy(moe_handle_t h) {
+  if (!valid_handle(h)) return MOE_ERR_INVALID_ARG;
+  h->magic = 0;
+  delete h;
+  return MOE_OK;
+}
+
+int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K, int E,
+               int P, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_handle(h)) return MOE_ERR_INVALID_ARG;
+  const int st = check_shape(T, K, E, P);
+  if (st != MOE_OK) return st;
+  if (itype != MOE_I32 && itype != MOE_I64) return MOE_ERR_UNSUPPORTED;
+  if (!workspace || (T > 0 && !topk_idx)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return MOE_ERR_ALIGNMENT;
+  if (T > 0 && !aligned(topk_idx, itype == MOE_I32 ? 4 : 8)) return MOE_ERR_ALIGNMENT;
+  const moe::WsLayout plan = moe::plan_workspace(T, K, E, P);
+  if (workspace_bytes < plan.total) return MOE_ERR_WORKSPACE;
+
+  h->has_layout = false;
+  h->T = T;
+  h->K = K;
+  h->E = E;
+  h->P = P;
+  h->ws = static_cast<char*>(workspace);
+  h->plan = plan;
+
+  moe::LayoutArgs a{};
+  a.idx = topk_idx;
+  a.itype = itype;
+  a.T = (int)T;
+  a.K = K;
+  a.E = E;
+  a.P = P;
+  a.epr = E / P;
+  a.nblk = plan.nblk;
+  a.tile = plan.tile;
+  a.ehist = ws_ptr<int>(h, plan.ehist);
+  a.rhist = ws_ptr<int>(h, plan.rhist);
+  a.tok_mask = ws_ptr<unsigned long long>(h, plan.tok_mask);
+  a.num_tokens_per_expert = ws_ptr<int>(h, plan.num_tokens_per_expert);
+  a.num_tokens_per_rank = ws_ptr<int>(h, plan.num_tokens_per_rank);
+  a.is_token_in_rank = ws_ptr<uint8_t>(h, plan.is_token_in_rank);
+  a.expert_offset = ws_ptr<int>(h, plan.expert_offset);
+  a.rank_offset = ws_ptr<int>(h, plan.rank_offset);
+  a.send_offset = ws_ptr<int>(h, plan.send_offset);
+  a.token_slot = ws_ptr<int>(h, plan.token_slot);
+  a.recv_pos = ws_ptr<int>(h, plan.recv_pos);
+  a.recv_token = ws_ptr<int>(h, plan.recv_token);
+  a.recv_k = ws_ptr<int>(h, plan.recv_k);
+  a.status = ws_ptr<int>(h, plan.status);
+  const int rc = hip_status(moe::launch_layout(a, stream));
+  if (rc == MOE_OK) h->has_layout = true;
+  return rc;
+}
+
+int moe_dispatch(moe_handle_t h, const void* x, int dtype, int64_t H, const float* topk_weights,
+                 int scale_rows, void* recv, float* recv_scores, hipStream_t stream) {
+  int NV = 0;
+  const int st = check_rows(h, dtype, H, &NV);
+  if (st != MOE_OK) return st;
+  if (scale_rows != 0 && scale_rows != 1) return MOE_ERR_INVALID_ARG;
+  if ((scale_rows || recv_scores) && !topk_weights) return MOE_ERR_INVALID_ARG;
+  if (h->T == 0) return MOE_OK;
+  if (!x || !recv) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(recv, 16)) return MOE_ERR_ALIGNMENT;
+  if ((topk_weights && !aligned(topk_weights, 4)) || (recv_scores && !aligned(recv_scores, 4)))
+    return MOE_ERR_ALIGNMENT;
+  moe::ScatterArgs a{};
+  a.src = x;
+  a.recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
+  a.w = topk_weights;
+  a.dst = recv;
+  a.scores_out = recv_scores;
+  a.T = (int)h->T;
+  a.K = h->K;
+  a.NV = NV;
+  a.R = (int)(h->T * h->K);
+  a.dtype = dtype;
+  a.scale = scale_rows != 0;
+  a.status = ws_ptr<int>(h, h->plan.status);
+  return hip_status(moe::launch_scatter(a, h->tune, stream));
+}
+
+int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H, const float* topk_weights,
+                void* out, hipStream_t stream) {
+  int NV = 0;
+  const int st = check_rows(h, dtype, H, &NV);
+  if (st != MOE_OK) return st;
+  if (h->T == 0) return MOE_OK;
+  if (!y || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
+  if (topk_weights && !aligned(topk_weights, 4)) return MOE_ERR_ALIGNMENT;
+  moe::GatherArgs a{};
+  a.src = y;
+  a.recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
+  a.w = topk_weights;
+  a.dst = out;
+  a.T = (int)h->T;
+  a.K = h->K;
+  a.NV = NV;
+  a.R = (int)(h->T * h->K);
+  a.dtype = dtype;
+  a.status = ws_ptr<int>(h, h->plan.status);
+  moe::Tuning t = h->tune;
+  t.chunks_per_lane = t.chunks_per_lane >= 4 ? 2 : t.chunks_per_lane;  // gather keeps K rows live
+  return hip_status(moe::launch_gather(a, t, stream));
+}
+
+int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
+                    const float* topk_weights, const void* y, void* grad_y, float* grad_w,
+                    hipStream_t stream) {
+  int NV = 0;
+  const int st = check_rows(h, dtype, H, &NV);
+  if (st != MOE_OK) return st;
+  if (grad_w && (!topk_weights || !y)) return MOE_ERR_INVALID_ARG;
+  if (h->T == 0) return MOE_OK;
+  if (!grad_out || !grad_y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(grad_out, 16) || !aligned(grad_y, 16) || (grad_w && !aligned(y, 16)))
+    return MOE_ERR_ALIGNMENT;
+  if ((topk_weights && !aligned(topk_weights, 4)) || (grad_w && !aligned(grad_w, 4)))
+    return MOE_ERR_ALIGNMENT;
+  moe::ScatterArgs a{};
+  a.src = grad_out;
+  a.recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
+  a.w = topk_weights;
+  a.dst = grad_y;
+  a.other = grad_w ? y : nullptr;
+  a.dot_out = grad_w;
+  a.T = (int)h->T;
+  a.K = h->K;
+  a.NV = NV;
+  a.R = (int)(h->T * h->K);
+  a.dtype = dtype;
+  a.scale = topk_weights != nullptr;
+  a.status = ws_ptr<int>(h, h->plan.status);
+  moe::Tuning t = h->tune;
+  if (grad_w && t.chunks_per_lane >= 4) t.chunks_per_lane = 2;  // dot keeps K rows live
+  return hip_status(moe::launch_scatter(a, t, stream));
+}
+
+int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H,
+                     const float* topk_weights, const void* x, void* grad_x, float* grad_s,
+                     hipStream_t stream) {
+  int NV = 0;
+  const int st = check_rows(h, dtype, H, &NV);
+  if (st != MOE_OK) return st;
+  if (grad_s && (!topk_weights || !x)) return MOE_ERR_INVALID_ARG;
+  if (h->T == 0) return MOE_OK;
+  if (!grad_recv || !grad_x) return MOE_ERR_INVALID_ARG;
+  if (!aligned(grad_recv, 16) || !aligned(grad_x, 16) || (grad_s && !aligned(x, 16)))
+    return MOE_ERR_ALIGNMENT;
+  if ((topk_weights && !aligned(topk_weights, 4)) || (grad_s && !aligned(grad_s, 4)))
+    return MOE_ERR_ALIGNMENT;
+  moe::GatherArgs a{};
+  a.src = grad_recv;
+  a.recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
+  a.w = topk_weights;
+  a.dst = grad_x;
+  a.other = grad_s ? x : nullptr;
+  a.dot_out = grad_s;
+  a.T = (int)h->T;
+  a.K = h->K;
+  a.NV = NV;
+  a.R = (int)(h->T * h->K);
+  a.dtype = dtype;
+  a.status = ws_ptr<int>(h, h->plan.status);
+  moe::Tuning t = h->tune;
+  t.chunks_per_lane = t.chunks_per_lane >= 4 ? 2 : t.chunks_per_lane;
+  return hip_status(moe::launch_gather(a, t, stream));
+}
+
+int moe_handle_field(moe_handle_t h, int field, void** dev_ptr, size_t* bytes) {
+  if (!valid_handle(h) || !dev_ptr || !bytes) return MOE_ERR_INVALID_ARG;
+  if (!h->has_layout) return MOE_ERR_HANDLE;
+  const moe::WsLayout& p = h->plan;
+  const size_t T = (size_t)h->T, K = (size_t)h->K, E = (size_t)h->E, P = (size_t)h->P;
+  size_t off = 0, n = 0;
+  switch (field) {
+    case MOE_FIELD_NUM_TOKENS_PER_EXPERT: off = p.num_tokens_per_expert; n = E * 4; break;
+    case MOE_FIELD_NUM_TOKENS_PER_RANK: off = p.num_tokens_per_rank; n = P * 4; break;
+    case MOE_FIELD_IS_TOKEN_IN_RANK: off = p.is_token_in_rank; n = T * P; break;
+    case MOE_FIELD_EXPERT_OFFSET: off = p.expert_offset; n = (E + 1) * 4; break;
+    case MOE_FIELD_RANK_OFFSET: off = p.rank_offset; n = (P + 1) * 4; break;
+    case MOE_FIELD_SEND_OFFSET: off = p.send_offset; n = (P + 1) * 4; break;
+    case MOE_FIELD_TOKEN_SLOT: off = p.token_slot; n = T * P * 4; break;
+    case MOE_FIELD_RECV_POS: off = p.recv_pos; n = T * K * 4; break;
+    case MOE_FIELD_RECV_TOKEN: off = p.recv_token; n = T * K * 4; break;
+    case MOE_FIELD_RECV_K: off = p.recv_k; n = T * K * 4; break;
+    case MOE_FIELD_STATUS: off = p.status; n = 4; break;
+    default: return MOE_ERR_INVALID_ARG;
+  }
+  *dev_ptr = h->ws + off;
+  *bytes = n;
+  return MOE_OK;
+}
+
+int moe_handle_dims(moe_handle_t h, int64_t* T, int* K, int* E, int* P) {
+  if (!valid_handle(h) || !T || !K || !E || !P) return MOE_ERR_INVALID_ARG;
+  if (!h->has_layout) return MOE_ERR_HANDLE;
+  *T = h->T;
+  *K = h->K;
+  *E = h->E;
+  *P = h->P;
+  return MOE_OK;
+}
+
+int moe_handle_check(moe_handle_t h, hipStream_t stream, int* device_status) {
+  if (!valid_handle(h) || !device_status) return MOE_ERR_INVALID_ARG;
+  if (!h->has_layout) return MOE_ERR_HANDLE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, h->ws + h->plan.status, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return MOE_ERR_HIP;
+  *device_status = v;
+  return MOE_OK;
+}
+
+int moe_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (!dst || !src) return MOE_ERR_INVALID_ARG;
+  if (bytes % 16 != 0) return MOE_ERR_SHAPE;
+  if (!aligned(dst, 16) || !aligned(src, 16)) return MOE_ERR_ALIGNMENT;
+  return hip_status(moe::launch_copy(dst, src, bytes, stream));
+}
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or missing companion argument)";
+    case MOE_ERR_SHAPE: return "invalid shape (K<1, K>E, E%P!=0, H<1 or a row that is not whole 16-byte chunks)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported (dtype/itype, P>64, E>1024, K>32 or T*K>=2^31)";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer (rows need 16 bytes, workspace 256)";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
+    case MOE_ERR_HANDLE: return "bad handle, or a row call before moe_layout";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_version(void) { return "moe_layout 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal interface between the C ABI (abi.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Workspace sections (byte offsets from the workspace base, 256-aligned).
+struct WsLayout {
+  size_t status, num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
+      expert_offset, rank_offset, send_offset, token_slot, recv_pos, recv_token,
+      recv_k, tok_mask, ehist, rhist;
+  size_t total;
+  int nblk;  // layout workgroups
+  int tile;  // tokens per layout workgroup
+};
+
+WsLayout plan_workspace(int64_t T, int K, int E, int P);
+
+struct LayoutArgs {
+  const void* idx;
+  int itype, T, K, E, P, epr, nblk, tile;
+  int* ehist;             // [E+1][nblk], expert-major
+  int* rhist;             // [P][nblk], partition-major
+  unsigned long long* tok_mask;  // [T]
+  int* num_tokens_per_expert;
+  int* num_tokens_per_rank;
+  uint8_t* is_token_in_rank;
+  int* expert_offset;
+  int* rank_offset;
+  int* send_offset;
+  int* token_slot;
+  int* recv_pos;
+  int* recv_token;
+  int* recv_k;
+  int* status;
+};
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
+
+// Token-row -> receive-row direction (dispatch, combine backward).
+struct ScatterArgs {
+  const void* src;        // [T, NV] chunks
+  const int* recv_pos;    // [T, K]
+  const float* w;         // [T, K] or null
+  void* dst;              // [R, NV] chunks
+  float* scores_out;      // [R] or null
+  const void* other;      // [R, NV] chunks (dot operand) or null
+  float* dot_out;         // [T, K] or null
+  int T, K, NV, R;
+  int dtype;
+  bool scale;             // dst = round(w * src)
+  int* status;
+};
+
+// Receive-row -> token-row direction (combine, dispatch backward).
+struct GatherArgs {
+  const void* src;        // [R, NV] chunks
+  const int* recv_pos;    // [T, K]
+  const float* w;         // [T, K] or null (plain sum)
+  void* dst;              // [T, NV] chunks
+  const void* other;      // [T, NV] chunks (dot operand) or null
+  float* dot_out;         // [T, K] or null
+  int T, K, NV, R;
+  int dtype;
+  int* status;
+};
+
+struct Tuning {
+  int chunks_per_lane;  // 1, 2, 4
+  int nontemporal;      // 0, 1, 2
+  int waves_per_block;  // 1, 2, 4, 8
+};
+
+hipError_t launch_scatter(const ScatterArgs& a, const Tuning& t, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, const Tuning& t, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+}  // namespace moe

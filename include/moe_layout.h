@@ -1,0 +1,209 @@
+/*
+ * moe_layout.h -- C ABI of the MI355X (gfx950) MoE token layout / dispatch /
+ * combine library (libmoe_layout.so).
+ *
+ * What it computes is the data-parallel hot path of expert-parallel token
+ * exchange, on one GPU: the P expert-parallel ranks are P virtual partitions
+ * of one receive buffer in HBM.
+ *
+ *   "Add an opt-in DeepEP transport for the AutoEP expert all-to-all"
+ *   (DeepSpeed PR), sections "Why" and "Scope and safety": dispatch takes the
+ *   tokens before top-k expansion together with topk_idx / topk_weights,
+ *   copies each token once to every rank that hosts one of its experts,
+ *   groups the arrivals by expert, and returns a handle; combine reduces the
+ *   weighted sum back to token order.  The backward of a combine is a
+ *   dispatch and the backward of a dispatch is a combine, both run with the
+ *   forward dispatch's handle.  The review fix on the same page adds that
+ *   dispatch returns the received weights and that both backward passes
+ *   return the router-weight gradient.
+ *
+ *   "[MoE] Apply router scores before W2 projection" (torchtitan), sections
+ *   "Motivation" and "Implementation": with the scores absorbed, dispatch
+ *   also returns the per-row scores in the rows' expert-major order, the
+ *   rows are scaled in float32 and cast back, and combine is a plain sum.
+ *
+ * Conventions (every entry point):
+ *   - All tensor pointers are DEVICE pointers; the caller owns every buffer,
+ *     the workspace and the stream.  Row-major, contiguous.
+ *   - Calls are stream-ordered on `stream` and never block the host, except
+ *     moe_handle_check, which synchronises the stream.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call launches nothing and returns a negative MOE_ERR_* code.
+ *   - T = tokens, K = top-k, E = experts, P = partitions (virtual EP ranks),
+ *     H = row width in elements, R = T*K receive rows.
+ *   - Expert e belongs to partition e / (E/P); E must be a multiple of P.
+ *   - Element types: MOE_F32 (float) or MOE_BF16 (bfloat16 bits).  Every
+ *     row is a whole number of 16-byte chunks: H*sizeof(elem) % 16 == 0.
+ *   - Floating-point contract: products and sums in IEEE float32, each
+ *     rounded on its own (no fused multiply-add); sums over k run in k order
+ *     from +0.0; bfloat16 results are rounded to nearest, ties to even.
+ *     Router-weight gradients use a fixed 64-partial order (see
+ *     moe_combine_bwd), so results are bitwise reproducible.
+ */
+#ifndef MOE_LAYOUT_H
+#define MOE_LAYOUT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK                 0
+#define MOE_ERR_INVALID_ARG   -1  /* null pointer, negative size, missing companion argument */
+#define MOE_ERR_SHAPE         -2  /* K < 1, K > E, E % P != 0, H*elem % 16 != 0, H < 1 */
+#define MOE_ERR_UNSUPPORTED   -3  /* unknown dtype/itype, P > 64, E > 1024, K > 32, T*K >= 2^31 */
+#define MOE_ERR_ALIGNMENT     -4  /* row pointers not 16-byte aligned, others not elem-aligned */
+#define MOE_ERR_WORKSPACE     -5  /* workspace smaller than moe_workspace_size() */
+#define MOE_ERR_HANDLE        -6  /* bad handle, or a data call before moe_layout */
+#define MOE_ERR_HIP           -7  /* a HIP runtime call failed */
+
+/* ---- element and index types ------------------------------------------- */
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+enum moe_itype { MOE_I32 = 0, MOE_I64 = 1 };
+
+/* ---- limits -------------------------------------------------------------- */
+#define MOE_MAX_K 32
+#define MOE_MAX_E 1024
+#define MOE_MAX_P 64
+
+/* ---- device status bits (read with moe_handle_check) --------------------- */
+#define MOE_STATUS_BAD_EXPERT   1  /* a topk_idx entry outside [0, E) */
+#define MOE_STATUS_BAD_POSITION 2  /* a data kernel met a receive row outside [0, R) */
+
+/* ---- handle fields (moe_handle_field) ------------------------------------ */
+enum moe_field {
+  MOE_FIELD_NUM_TOKENS_PER_EXPERT = 0, /* int32 [E]   (t,k) pairs per expert               */
+  MOE_FIELD_NUM_TOKENS_PER_RANK   = 1, /* int32 [P]   distinct tokens per partition         */
+  MOE_FIELD_IS_TOKEN_IN_RANK      = 2, /* uint8 [T,P] 1 if any of t's experts is on r       */
+  MOE_FIELD_EXPERT_OFFSET         = 3, /* int32 [E+1] exclusive prefix of expert counts     */
+  MOE_FIELD_RANK_OFFSET           = 4, /* int32 [P+1] first receive row of each partition   */
+  MOE_FIELD_SEND_OFFSET           = 5, /* int32 [P+1] exclusive prefix of num_tokens_per_rank */
+  MOE_FIELD_TOKEN_SLOT            = 6, /* int32 [T,P] t's slot in r's send list, or -1      */
+  MOE_FIELD_RECV_POS              = 7, /* int32 [T,K] receive row of pair (t,k)            */
+  MOE_FIELD_RECV_TOKEN            = 8, /* int32 [R]   token of each receive row            */
+  MOE_FIELD_RECV_K                = 9, /* int32 [R]   k of each receive row                */
+  MOE_FIELD_STATUS                = 10 /* int32 [1]   device status bits                   */
+};
+
+/* Optional launch knobs; zero means "library default". */
+typedef struct moe_tuning {
+  int chunks_per_lane;  /* 16-byte chunks each lane keeps in flight per row: 0, 1, 2 or 4 */
+  int nontemporal;      /* 0: default stores; 1: receive-row stores marked non-temporal;
+                           2: all row stores marked non-temporal                          */
+  int waves_per_block;  /* tokens (one wave each) per workgroup: 0, 1, 2, 4, 8           */
+} moe_tuning;
+
+typedef struct moe_handle_s* moe_handle_t;
+
+/* Bytes of device workspace a layout of this shape needs (pure host).
+ * Returns MOE_ERR_* on an invalid shape (same rules as moe_layout). */
+int moe_workspace_size(int64_t T, int K, int E, int P, size_t* bytes);
+
+/* Create / destroy a handle.  `tuning` may be NULL.  Host memory only: the
+ * handle records views into the caller's workspace, never owns device memory. */
+int moe_handle_create(moe_handle_t* out, const moe_tuning* tuning);
+int moe_handle_destroy(moe_handle_t h);
+
+/* Layout of one routing decision (method steps: counts, offsets, stable
+ * positions).  Fills every handle field inside `workspace`.
+ *
+ *   topk_idx   [T,K] int32 (itype MOE_I32) or int64 (MOE_I64), device.
+ *   workspace  device, >= moe_workspace_size(T,K,E,P) bytes, 256-byte aligned;
+ *              it holds the handle's arrays and must outlive every later call
+ *              on this handle.
+ *
+ * Definitions (oracle: stable counting sort of the (t,k) pairs by expert):
+ *   recv_pos[t,k] = expert_offset[e] + #{(t',k') < (t,k) lexicographically
+ *                    with topk_idx[t',k'] == e},  e = topk_idx[t,k];
+ *   so rows are grouped by expert in ascending id (hence by partition), and
+ *   inside an expert by token, then k.  The order depends on the routing
+ *   only, so an activation-checkpoint replay of the same routing reproduces
+ *   every position ("perf(dllm): use the DeepEP dispatcher in the
+ *   DiffusionGemma recipes", section "Why hybridep + activation
+ *   checkpointing fails", shows what a replay-nondeterministic dispatch does).
+ *   token_slot[t,r] numbers the tokens with is_token_in_rank[t,r] in
+ *   increasing t (a token is sent once per partition, not once per expert:
+ *   the deduplication of the DeepSpeed transport PR's "Why" section).
+ *
+ * T = 0 is valid and yields an empty layout.  Entries of topk_idx outside
+ * [0,E) are an input error detected on the device: MOE_STATUS_BAD_EXPERT is
+ * set and those pairs are placed after the last expert's rows (so every
+ * position stays inside [0,R)); the other fields are then unspecified.
+ * Duplicate ids within a token are accepted and ordered by k.
+ * The handle must not be used on two streams at once.                      */
+int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K,
+               int E, int P, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/* Forward dispatch: recv[recv_pos[t,k], :] = x[t, :].
+ *
+ *   x             [T,H] dtype, 16-byte aligned.
+ *   topk_weights  [T,K] float32 or NULL; required when scale_rows or
+ *                 recv_scores is given.
+ *   scale_rows    0: copy rows bit for bit.  1: scores absorbed before W2,
+ *                 recv = round(float32(x[t]) * w[t,k]).
+ *   recv          [R,H] dtype, 16-byte aligned (output).
+ *   recv_scores   [R] float32 or NULL (output): recv_scores[recv_pos[t,k]] = w[t,k].
+ * Each x row is read once and stored to its receive rows partition by
+ * partition.                                                              */
+int moe_dispatch(moe_handle_t h, const void* x, int dtype, int64_t H,
+                 const float* topk_weights, int scale_rows, void* recv,
+                 float* recv_scores, hipStream_t stream);
+
+/* Forward combine: out[t] = round(sum_k w[t,k] * y[recv_pos[t,k]]), or the
+ * plain sum when topk_weights is NULL (scores absorbed).  float32, k order.
+ *   y [R,H], out [T,H] dtype, 16-byte aligned.                             */
+int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H,
+                const float* topk_weights, void* out, hipStream_t stream);
+
+/* Backward of moe_combine (a dispatch of the output gradient):
+ *   grad_y[recv_pos[t,k]] = round(w[t,k] * grad_out[t])  (copy if no weights)
+ *   grad_w[t,k] = <grad_out[t], y[recv_pos[t,k]]>        (if grad_w != NULL)
+ * grad_w needs topk_weights and y.  The dot product is float32 in a fixed
+ * order: row cut into 16-byte chunks, chunk j added (element by element,
+ * product rounded then sum rounded) into partial j mod 64, the 64 partials
+ * then folded L[l] += L[l xor s] for s = 32,16,8,4,2,1; result = partial 0.
+ *   grad_out [T,H], y [R,H], grad_y [R,H] dtype; grad_w [T,K] float32.     */
+int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
+                    const float* topk_weights, const void* y, void* grad_y,
+                    float* grad_w, hipStream_t stream);
+
+/* Backward of moe_dispatch (a combine of the receive-row gradient):
+ *   grad_x[t] = round(sum_k [w[t,k] *] grad_recv[recv_pos[t,k]])
+ *   grad_s[t,k] = <grad_recv[recv_pos[t,k]], x[t]>        (if grad_s != NULL)
+ * Pass topk_weights iff the forward dispatch scaled its rows (the scaling is
+ * differentiated straight through its rounding).  grad_s needs topk_weights
+ * and x; same dot order as moe_combine_bwd.
+ *   grad_recv [R,H], x [T,H], grad_x [T,H] dtype; grad_s [T,K] float32.   */
+int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H,
+                     const float* topk_weights, const void* x, void* grad_x,
+                     float* grad_s, hipStream_t stream);
+
+/* Device pointer and byte size of one handle field (no synchronisation). */
+int moe_handle_field(moe_handle_t h, int field, void** dev_ptr, size_t* bytes);
+
+/* Shape recorded by the last moe_layout on this handle. */
+int moe_handle_dims(moe_handle_t h, int64_t* T, int* K, int* E, int* P);
+
+/* Synchronises `stream`, then reads the device status word (MOE_STATUS_* bits). */
+int moe_handle_check(moe_handle_t h, hipStream_t stream, int* device_status);
+
+/* Plain device copy of `bytes` (multiple of 16, 16-byte aligned pointers):
+ * the reference kernel for calibrating HBM traffic counters against a known
+ * byte count.  Not part of the method.                                    */
+int moe_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+/* Message for a status code (static string). */
+const char* moe_strerror(int status);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LAYOUT_H */

@@ -1,0 +1,148 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and host validation rejects bad arguments with the exact
+status codes before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_layout.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from combine_moe_layout_04_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from combine_moe_layout_04_amd.build import build
+        build()
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def codes():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(MOE_(?:OK|ERR_\w+))\s+(-?\d+)", text)}
+
+
+C = codes()
+FAKE = 1 << 20          # a 256-aligned address that validation never dereferences
+
+
+def test_header_declares_the_method_entry_points():
+    names = declared_functions()
+    for n in ("moe_layout", "moe_dispatch", "moe_combine", "moe_dispatch_bwd", "moe_combine_bwd",
+              "moe_handle_create", "moe_handle_destroy", "moe_workspace_size"):
+        assert n in names
+
+
+def test_every_declared_function_is_exported(L):
+    from combine_moe_layout_04_amd._lib import LIB_PATH, SIGNATURES
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)$", out, re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert n in SIGNATURES, n
+        getattr(L, n)
+
+
+def test_workspace_size_rules(L):
+    n = ctypes.c_size_t()
+    f = L.moe_workspace_size
+    assert f(4096, 8, 128, 8, ctypes.byref(n)) == C["MOE_OK"] and n.value > 0
+    big = n.value
+    assert f(1024, 8, 128, 8, ctypes.byref(n)) == C["MOE_OK"] and n.value < big
+    assert f(0, 8, 128, 8, ctypes.byref(n)) == C["MOE_OK"] and n.value > 0
+    assert f(-1, 8, 128, 8, ctypes.byref(n)) == C["MOE_ERR_INVALID_ARG"]
+    assert f(16, 0, 128, 8, ctypes.byref(n)) == C["MOE_ERR_SHAPE"]
+    assert f(16, 33, 128, 8, ctypes.byref(n)) == C["MOE_ERR_UNSUPPORTED"]
+    assert f(16, 8, 130, 8, ctypes.byref(n)) == C["MOE_ERR_SHAPE"]
+    assert f(16, 8, 128, 128, ctypes.byref(n)) == C["MOE_ERR_UNSUPPORTED"]
+    assert f(16, 8, 2048, 8, ctypes.byref(n)) == C["MOE_ERR_UNSUPPORTED"]
+    assert f(16, 9, 8, 8, ctypes.byref(n)) == C["MOE_ERR_SHAPE"]
+    assert f(1 << 29, 8, 128, 8, ctypes.byref(n)) == C["MOE_ERR_UNSUPPORTED"]
+    assert f(16, 8, 128, 8, None) == C["MOE_ERR_INVALID_ARG"]
+
+
+def test_workspace_holds_the_handle_arrays(L):
+    # T*K positions, two inverse maps, T*P slots and flags, counts and offsets
+    n = ctypes.c_size_t()
+    T, K, E, P = 4096, 8, 256, 64
+    assert L.moe_workspace_size(T, K, E, P, ctypes.byref(n)) == 0
+    lower = 3 * T * K * 4 + T * P * 5 + (2 * E + 3 * P) * 4
+    assert lower <= n.value <= lower + (1 << 20)
+
+
+def test_handle_lifecycle_and_tuning(L):
+    from combine_moe_layout_04_amd._lib import MoeTuning
+    h = ctypes.c_void_p()
+    assert L.moe_handle_create(ctypes.byref(h), None) == C["MOE_OK"] and h.value
+    assert L.moe_handle_destroy(h) == C["MOE_OK"]
+    assert L.moe_handle_destroy(None) == C["MOE_ERR_INVALID_ARG"]
+    assert L.moe_handle_create(None, None) == C["MOE_ERR_INVALID_ARG"]
+    for bad in (MoeTuning(3, 0, 0), MoeTuning(0, 3, 0), MoeTuning(0, 0, 3)):
+        assert L.moe_handle_create(ctypes.byref(h), ctypes.byref(bad)) == C["MOE_ERR_INVALID_ARG"]
+    good = MoeTuning(2, 2, 8)
+    assert L.moe_handle_create(ctypes.byref(h), ctypes.byref(good)) == C["MOE_OK"]
+    assert L.moe_handle_destroy(h) == C["MOE_OK"]
+
+
+@pytest.fixture
+def handle(L):
+    h = ctypes.c_void_p()
+    assert L.moe_handle_create(ctypes.byref(h), None) == 0
+    yield h
+    L.moe_handle_destroy(h)
+
+
+def test_layout_validation_codes(L, handle):
+    f = L.moe_layout
+    ws = ctypes.c_void_p(FAKE)
+    idx = ctypes.c_void_p(FAKE)
+    need = ctypes.c_size_t()
+    L.moe_workspace_size(64, 8, 128, 8, ctypes.byref(need))
+    big = need.value
+    assert f(None, idx, 0, 64, 8, 128, 8, ws, big, None) == C["MOE_ERR_INVALID_ARG"]
+    assert f(handle, idx, 0, -1, 8, 128, 8, ws, big, None) == C["MOE_ERR_INVALID_ARG"]
+    assert f(handle, idx, 0, 64, 0, 128, 8, ws, big, None) == C["MOE_ERR_SHAPE"]
+    assert f(handle, idx, 0, 64, 8, 130, 8, ws, big, None) == C["MOE_ERR_SHAPE"]
+    assert f(handle, idx, 0, 64, 8, 128, 65, ws, big, None) == C["MOE_ERR_UNSUPPORTED"]
+    assert f(handle, idx, 2, 64, 8, 128, 8, ws, big, None) == C["MOE_ERR_UNSUPPORTED"]
+    assert f(handle, None, 0, 64, 8, 128, 8, ws, big, None) == C["MOE_ERR_INVALID_ARG"]
+    assert f(handle, idx, 0, 64, 8, 128, 8, None, big, None) == C["MOE_ERR_INVALID_ARG"]
+    assert f(handle, idx, 0, 64, 8, 128, 8, ctypes.c_void_p(FAKE + 64), big, None) == C["MOE_ERR_ALIGNMENT"]
+    assert f(handle, ctypes.c_void_p(FAKE + 2), 0, 64, 8, 128, 8, ws, big, None) == C["MOE_ERR_ALIGNMENT"]
+    assert f(handle, ctypes.c_void_p(FAKE + 4), 1, 64, 8, 128, 8, ws, big, None) == C["MOE_ERR_ALIGNMENT"]
+    assert f(handle, idx, 0, 64, 8, 128, 8, ws, big - 1, None) == C["MOE_ERR_WORKSPACE"]
+
+
+def test_row_calls_need_a_layout(L, handle):
+    p = ctypes.c_void_p(FAKE)
+    assert L.moe_dispatch(handle, p, 1, 2048, None, 0, p, None, None) == C["MOE_ERR_HANDLE"]
+    assert L.moe_combine(handle, p, 1, 2048, None, p, None) == C["MOE_ERR_HANDLE"]
+    assert L.moe_combine_bwd(handle, p, 1, 2048, None, None, p, None, None) == C["MOE_ERR_HANDLE"]
+    assert L.moe_dispatch_bwd(handle, p, 1, 2048, None, None, p, None, None) == C["MOE_ERR_HANDLE"]
+    assert L.moe_dispatch(None, p, 1, 2048, None, 0, p, None, None) == C["MOE_ERR_INVALID_ARG"]
+    dp, n = ctypes.c_void_p(), ctypes.c_size_t()
+    assert L.moe_handle_field(handle, 7, ctypes.byref(dp), ctypes.byref(n)) == C["MOE_ERR_HANDLE"]
+    st = ctypes.c_int()
+    assert L.moe_handle_check(handle, None, ctypes.byref(st)) == C["MOE_ERR_HANDLE"]
+
+
+def test_copy_validation(L):
+    p = ctypes.c_void_p(FAKE)
+    assert L.moe_bench_copy(p, p, 15, None) == C["MOE_ERR_SHAPE"]
+    assert L.moe_bench_copy(ctypes.c_void_p(FAKE + 8), p, 16, None) == C["MOE_ERR_ALIGNMENT"]
+    assert L.moe_bench_copy(None, p, 16, None) == C["MOE_ERR_INVALID_ARG"]
+
+
+def test_strerror_and_version(L):
+    for name, code in C.items():
+        assert L.moe_strerror(code)
+    assert b"gfx950" in L.moe_version()

@@ -1,0 +1,377 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: layout, handle and dispatch bit-exact; combine and backward outputs
+within max-abs 1e-6 (float32) or 1 bf16 ulp (bfloat16) of the oracle, which
+accumulates in float32 in the same k order.  The float32 contract (separate
+roundings, k order, canonical dot order) makes zero difference the expected
+result, so every test also asserts bitwise equality.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import combine_moe_layout_04_amd as M
+from oracle import moe_oracle as O
+
+from devutil import as_f64, assert_f32_close, assert_rows_close, n_diff, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+LAYOUT_FIELDS = ["num_tokens_per_expert", "num_tokens_per_rank", "is_token_in_rank",
+                 "expert_offset", "rank_offset", "send_offset", "token_slot",
+                 "recv_pos", "recv_token", "recv_k"]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check_layout(h, lay):
+    for f in LAYOUT_FIELDS:
+        got = h.field(f).cpu().numpy()
+        ref = np.asarray(getattr(lay, f))
+        assert got.shape == ref.shape, (f, got.shape, ref.shape)
+        assert np.array_equal(got, ref.astype(got.dtype)), f"{f}: {n_diff(got, ref)} entries differ"
+
+
+def run_layer(cfg, inp, h=None, tuning=None):
+    """Forward + backward through the library; returns host copies."""
+    dt = cfg.dtype
+    idx = torch.from_numpy(inp.topk_idx).to(DEV)
+    w = torch.from_numpy(inp.topk_weights).to(DEV)
+    x, y, g, gr = (to_dev(a, dt, DEV) for a in (inp.x, inp.y, inp.g, inp.grad_recv))
+    if h is None:
+        h = M.Handle(**(tuning or {}))
+    h = M.moe_layout(idx, cfg.E, cfg.P, handle=h)
+    res = {}
+    if cfg.absorbed:
+        recv, sc = M.moe_dispatch(h, x, w, scale_rows=True, recv_scores=True)
+        out = M.moe_combine(h, y)                       # plain sum
+        gy, gw = M.moe_combine_bwd(h, g)                # copy, no router gradient
+        gx, gs = M.moe_dispatch_bwd(h, gr, w, x, grad_s=True)
+    else:
+        recv, sc = M.moe_dispatch(h, x, w, recv_scores=True)
+        out = M.moe_combine(h, y, w)
+        gy, gw = M.moe_combine_bwd(h, g, w, y, grad_w=True)
+        gx, gs = M.moe_dispatch_bwd(h, gr)
+    status = h.check()
+    res.update(recv=to_host(recv, dt), scores=sc.cpu().numpy(), out=to_host(out, dt),
+               grad_y=to_host(gy, dt), grad_x=to_host(gx, dt),
+               grad_w=None if gw is None else gw.cpu().numpy(),
+               grad_s=None if gs is None else gs.cpu().numpy(), status=status)
+    return h, res
+
+
+def oracle_layer(cfg, inp):
+    dt = cfg.dtype
+    lay = O.layout(inp.topk_idx, cfg.E, cfg.P)
+    w = inp.topk_weights
+    ref = {}
+    if cfg.absorbed:
+        ref["recv"], ref["scores"] = O.dispatch(lay, inp.x, dt, w, scale_rows=True)
+        ref["out"] = O.combine(lay, inp.y, dt)
+        ref["grad_y"], ref["grad_w"] = O.combine_bwd(lay, inp.g, dt)
+        ref["grad_x"], ref["grad_s"] = O.dispatch_bwd(lay, inp.grad_recv, dt, w, inp.x)
+    else:
+        ref["recv"], ref["scores"] = O.dispatch(lay, inp.x, dt, w)
+        ref["out"] = O.combine(lay, inp.y, dt, w)
+        ref["grad_y"], ref["grad_w"] = O.combine_bwd(lay, inp.g, dt, w, inp.y)
+        ref["grad_x"], ref["grad_s"] = O.dispatch_bwd(lay, inp.grad_recv, dt)
+    return lay, ref
+
+
+def compare_layer(cfg, res, ref):
+    dt = cfg.dtype
+    assert res["status"] == 0, res["status"]
+    # dispatch: bit-exact (copies, or one rounding of one product when scaled)
+    assert np.array_equal(res["recv"], ref["recv"]), f"recv: {n_diff(res['recv'], ref['recv'])} differ"
+    assert np.array_equal(res["scores"], ref["scores"])
+    # combine / backward: the acceptance bar, then the bitwise contract
+    for k in ("out", "grad_y", "grad_x"):
+        assert_rows_close(res[k], ref[k], dt, k)
+    for k in ("grad_w", "grad_s"):
+        if ref[k] is None:
+            assert res[k] is None
+        else:
+            assert_f32_close(res[k], ref[k], k)
+    for k in ("out", "grad_y", "grad_x", "grad_w", "grad_s"):
+        if ref[k] is not None:
+            assert n_diff(res[k], ref[k]) == 0, f"{k}: {n_diff(res[k], ref[k])} elements not bit-identical"
+
+
+# ------------------------------------------------------------------ layout --
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_layout_full_size(name):
+    cfg = W.get_config(name)
+    say(f"layout {name} T={cfg.T} K={cfg.K} E={cfg.E} P={cfg.P}")
+    inp = W.layer_inputs(cfg, seed=0, with_rows=False)
+    h = M.moe_layout(torch.from_numpy(inp.topk_idx).to(DEV), cfg.E, cfg.P)
+    assert h.check() == 0
+    check_layout(h, O.layout(inp.topk_idx, cfg.E, cfg.P))
+
+
+def test_layout_int64_ids():
+    cfg = W.get_config("deepseek_v3")
+    inp = W.layer_inputs(cfg, seed=2, with_rows=False, idx_dtype=np.int64)
+    h = M.moe_layout(torch.from_numpy(inp.topk_idx).to(DEV), cfg.E, cfg.P)
+    assert h.check() == 0
+    check_layout(h, O.layout(inp.topk_idx, cfg.E, cfg.P))
+
+
+SMALL = [  # (T, K, E, P, distinct)
+    (1, 1, 1, 1, True), (1, 8, 8, 8, True), (63, 2, 8, 2, True), (64, 3, 12, 4, True),
+    (65, 4, 16, 16, True), (333, 8, 128, 8, True), (5000, 6, 64, 64, True),
+    (9000, 8, 256, 64, True), (700, 3, 5, 1, False), (129, 4, 4, 2, False),
+    (20000, 2, 1024, 64, True),
+]
+
+
+@pytest.mark.parametrize("T,K,E,P,distinct", SMALL)
+def test_layout_shapes(T, K, E, P, distinct):
+    say(f"layout T={T} K={K} E={E} P={P} distinct={distinct}")
+    rng = np.random.default_rng(T * 7 + K)
+    if distinct:
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    else:
+        idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    h = M.moe_layout(torch.from_numpy(idx).to(DEV), E, P)
+    assert h.check() == 0
+    check_layout(h, O.layout(idx, E, P))
+
+
+def test_layout_all_on_one_expert_and_empty_partitions():
+    T, K, E, P = 3000, 1, 64, 16
+    idx = np.full((T, K), 37, np.int32)
+    h = M.moe_layout(torch.from_numpy(idx).to(DEV), E, P)
+    assert h.check() == 0
+    check_layout(h, O.layout(idx, E, P))
+
+
+def test_layout_empty_batch():
+    h = M.moe_layout(torch.zeros((0, 4), dtype=torch.int32, device=DEV), 16, 4)
+    assert h.check() == 0
+    assert np.array_equal(h.field("expert_offset").cpu().numpy(), np.zeros(17, np.int32))
+    assert np.array_equal(h.field("send_offset").cpu().numpy(), np.zeros(5, np.int32))
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    recv, _ = M.moe_dispatch(h, x)
+    assert recv.shape == (0, 64)
+    assert M.moe_combine(h, recv).shape == (0, 64)
+
+
+def test_layout_is_deterministic_and_replays():
+    cfg = W.get_config("diffusion_gemma")
+    inp = W.layer_inputs(cfg, seed=3, with_rows=False)
+    idx = torch.from_numpy(inp.topk_idx).to(DEV)
+    h1 = M.moe_layout(idx, cfg.E, cfg.P)
+    a = h1.workspace.clone()
+    for _ in range(3):
+        h2 = M.moe_layout(idx.clone(), cfg.E, cfg.P)
+        for f in LAYOUT_FIELDS:
+            assert torch.equal(h1.field(f), h2.field(f)), f
+    assert torch.equal(a, h1.workspace)
+
+
+def test_invalid_ids_are_flagged_and_stay_in_bounds():
+    T, K, E, P = 500, 4, 32, 4
+    rng = np.random.default_rng(1)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    idx[7, 2] = E          # out of range
+    idx[100, 0] = -1       # dropped-token marker is also an error here
+    h = M.moe_layout(torch.from_numpy(idx).to(DEV), E, P)
+    assert h.check() & 1
+    pos = h.field("recv_pos").cpu().numpy()
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(T * K))   # still a bijection
+    eo = h.field("expert_offset").cpu().numpy()
+    assert eo[E] == T * K - 2                                        # valid pairs only
+    assert pos[7, 2] >= eo[E] and pos[100, 0] >= eo[E]
+
+
+# ---------------------------------------------------------------- full layer --
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_layer_full_size(name):
+    cfg = W.get_config(name)
+    say(f"layer {name} T={cfg.T} H={cfg.H} {cfg.dtype} E={cfg.E} P={cfg.P} K={cfg.K}")
+    inp = W.layer_inputs(cfg, seed=0)
+    h, res = run_layer(cfg, inp)
+    lay, ref = oracle_layer(cfg, inp)
+    check_layout(h, lay)
+    compare_layer(cfg, res, ref)
+
+
+RAGGED = [  # name, overrides
+    ("tiny", dict(T=37)),
+    ("tiny", dict(T=129, H=12)),
+    ("qwen3_30b_a3b", dict(T=70, H=40)),
+    ("qwen3_30b_a3b", dict(T=131, H=1032)),
+    ("diffusion_gemma", dict(T=67, H=520)),
+    ("deepseek_v3", dict(T=45, H=4104)),
+]
+
+
+@pytest.mark.parametrize("name,over", RAGGED)
+@pytest.mark.parametrize("tuning", [dict(), dict(chunks_per_lane=1, nontemporal=0, waves_per_block=1),
+                                    dict(chunks_per_lane=2, nontemporal=2, waves_per_block=8),
+                                    dict(chunks_per_lane=4, nontemporal=1, waves_per_block=2)])
+def test_layer_ragged_rows_all_tunings(name, over, tuning):
+    cfg = W.get_config(name, **over)
+    say(f"ragged {name} {over} {tuning}")
+    inp = W.layer_inputs(cfg, seed=5)
+    h, res = run_layer(cfg, inp, tuning=tuning)
+    _, ref = oracle_layer(cfg, inp)
+    compare_layer(cfg, res, ref)
+
+
+@pytest.mark.parametrize("absorbed", [False, True])
+@pytest.mark.parametrize("dtype,H", [("bf16", 264), ("f32", 132)])
+def test_k_above_one_group(absorbed, dtype, H):
+    # K = 12 > 8: rows go in two groups and the router gradient takes the
+    # separate pair-dot kernel; the results must not change.
+    base = W.get_config("qwen3_30b_a3b")
+    cfg = base.with_(T=150, H=H, dtype=dtype, E=24, P=4, K=12, absorbed=absorbed,
+                     renormalize=not absorbed)
+    say(f"K=12 absorbed={absorbed} {dtype} H={H}")
+    inp = W.layer_inputs(cfg, seed=9)
+    h, res = run_layer(cfg, inp)
+    _, ref = oracle_layer(cfg, inp)
+    compare_layer(cfg, res, ref)
+
+
+def test_unscaled_dispatch_with_scores_and_both_backward_modes():
+    cfg = W.get_config("qwen3_30b_a3b", T=300)
+    inp = W.layer_inputs(cfg, seed=4)
+    dt = cfg.dtype
+    idx = torch.from_numpy(inp.topk_idx).to(DEV)
+    w = torch.from_numpy(inp.topk_weights).to(DEV)
+    x, y, g, gr = (to_dev(a, dt, DEV) for a in (inp.x, inp.y, inp.g, inp.grad_recv))
+    h = M.moe_layout(idx, cfg.E, cfg.P)
+    lay = O.layout(inp.topk_idx, cfg.E, cfg.P)
+    # plain combine_bwd (copy) and weighted dispatch_bwd without grad_s
+    gy, gw = M.moe_combine_bwd(h, g)
+    assert gw is None
+    assert np.array_equal(to_host(gy, dt), O.combine_bwd(lay, inp.g, dt)[0])
+    gx, _ = M.moe_dispatch_bwd(h, gr, w)
+    assert np.array_equal(to_host(gx, dt), O.dispatch_bwd(lay, inp.grad_recv, dt, inp.topk_weights)[0])
+    # weighted combine_bwd without grad_w
+    gy2, _ = M.moe_combine_bwd(h, g, w)
+    assert np.array_equal(to_host(gy2, dt), O.combine_bwd(lay, inp.g, dt, inp.topk_weights)[0])
+    # scaled dispatch without scores
+    recv, sc = M.moe_dispatch(h, x, w, scale_rows=True)
+    assert sc is None
+    assert np.array_equal(to_host(recv, dt), O.dispatch(lay, inp.x, dt, inp.topk_weights, True)[0])
+    assert h.check() == 0
+
+
+def test_k_times_x_on_device():
+    cfg = W.get_config("qwen3_30b_a3b")
+    inp = W.layer_inputs(cfg, seed=6, with_rows=False)
+    x_np = W.normal_rows(cfg, cfg.T, 1, seed=6)
+    h = M.moe_layout(torch.from_numpy(inp.topk_idx).to(DEV), cfg.E, cfg.P)
+    recv, _ = M.moe_dispatch(h, to_dev(x_np, "bf16"))
+    out = M.moe_combine(h, recv)
+    assert np.array_equal(as_f64(to_host(out, "bf16"), "bf16"), cfg.K * as_f64(x_np, "bf16"))
+
+
+# ------------------------------------------------- absorbed-score protocol --
+
+def test_diffusion_gemma_three_passes_with_replay():
+    """Three forward passes per step with independent routings; passes 1 and
+    3 take a backward pass, each preceded by an activation-checkpoint replay
+    of layout + dispatch that must reproduce the forward bit for bit; the
+    combine is never replayed."""
+    cfg = W.get_config("diffusion_gemma")
+    dt = cfg.dtype
+    for pss in range(3):
+        say(f"diffusion_gemma pass {pss}")
+        inp = W.layer_inputs(cfg, seed=0, step=0, pss=pss)
+        idx = torch.from_numpy(inp.topk_idx).to(DEV)
+        w = torch.from_numpy(inp.topk_weights).to(DEV)
+        x = to_dev(inp.x, dt)
+        h = M.moe_layout(idx, cfg.E, cfg.P)
+        recv, sc = M.moe_dispatch(h, x, w, scale_rows=True, recv_scores=True)
+        out = M.moe_combine(h, recv)
+        lay = O.layout(inp.topk_idx, cfg.E, cfg.P)
+        r_recv, r_sc = O.dispatch(lay, inp.x, dt, inp.topk_weights, True)
+        assert np.array_equal(to_host(recv, dt), r_recv)
+        assert np.array_equal(sc.cpu().numpy(), r_sc)
+        assert np.array_equal(to_host(out, dt), O.combine(lay, r_recv, dt))
+        if pss == 1:
+            continue  # no-grad pass
+        h2 = M.moe_layout(idx.clone(), cfg.E, cfg.P)
+        recv2, sc2 = M.moe_dispatch(h2, x, w, scale_rows=True, recv_scores=True)
+        for f in LAYOUT_FIELDS:
+            assert torch.equal(h.field(f), h2.field(f)), f
+        assert torch.equal(recv.view(torch.int16), recv2.view(torch.int16))
+        assert torch.equal(sc, sc2)
+        g = to_dev(inp.g, dt)
+        gy, _ = M.moe_combine_bwd(h2, g)
+        gx, gs = M.moe_dispatch_bwd(h2, gy, w, x, grad_s=True)
+        r_gy, _ = O.combine_bwd(lay, inp.g, dt)
+        r_gx, r_gs = O.dispatch_bwd(lay, r_gy, dt, inp.topk_weights, inp.x)
+        assert np.array_equal(to_host(gy, dt), r_gy)
+        assert np.array_equal(to_host(gx, dt), r_gx)
+        assert np.array_equal(gs.cpu().numpy(), r_gs)
+        assert h2.check() == 0
+
+
+# ------------------------------------------------------- autograd wrappers --
+
+@pytest.mark.parametrize("absorbed", [False, True])
+def test_autograd_wrappers(absorbed):
+    from combine_moe_layout_04_amd import autograd as A
+    cfg = W.get_config("tiny", absorbed=absorbed, renormalize=not absorbed)
+    inp = W.layer_inputs(cfg, seed=11)
+    dt = cfg.dtype
+    idx = torch.from_numpy(inp.topk_idx).to(DEV)
+    w = torch.from_numpy(inp.topk_weights).to(DEV).requires_grad_(True)
+    x = to_dev(inp.x, dt).requires_grad_(True)
+    h = M.moe_layout(idx, cfg.E, cfg.P)
+    recv, _ = A.dispatch(x, w if absorbed else None, h, scale_rows=absorbed)
+    y = recv * 1.0  # identity expert, but a separate tensor
+    out = A.combine(y, None if absorbed else w, h)
+    g = to_dev(inp.g, dt)
+    out.backward(g)
+    lay = O.layout(inp.topk_idx, cfg.E, cfg.P)
+    wt = inp.topk_weights
+    r_recv, _ = O.dispatch(lay, inp.x, dt, wt, absorbed)
+    r_gy, r_gw = O.combine_bwd(lay, inp.g, dt, None if absorbed else wt, None if absorbed else r_recv)
+    r_gx, r_gs = O.dispatch_bwd(lay, r_gy, dt, wt if absorbed else None, inp.x if absorbed else None)
+    assert np.array_equal(to_host(x.grad, dt), r_gx)
+    assert w.grad is not None                     # the router keeps learning
+    assert np.array_equal(w.grad.cpu().numpy(), r_gs if absorbed else r_gw)
+
+
+# ----------------------------------------------------------- ABI on device --
+
+def test_row_call_validation_after_layout():
+    from combine_moe_layout_04_amd._lib import lib
+    import ctypes
+    L = lib()
+    idx = torch.zeros((8, 2), dtype=torch.int32, device=DEV)
+    idx[:, 1] = 1
+    h = M.moe_layout(idx, 4, 2)
+    p = ctypes.c_void_p(h.workspace.data_ptr())          # 256-aligned device memory
+    odd = ctypes.c_void_p(h.workspace.data_ptr() + 8)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.moe_dispatch(h.ptr, p, 2, 64, None, 0, p, None, s) == -3      # dtype
+    assert L.moe_dispatch(h.ptr, p, 1, 4, None, 0, p, None, s) == -2       # 8 bytes per row
+    assert L.moe_dispatch(h.ptr, p, 1, 0, None, 0, p, None, s) == -2
+    assert L.moe_dispatch(h.ptr, p, 1, 64, None, 1, p, None, s) == -1      # scale needs weights
+    assert L.moe_dispatch(h.ptr, p, 1, 64, None, 0, p, p, s) == -1         # scores need weights
+    assert L.moe_dispatch(h.ptr, odd, 1, 64, None, 0, p, None, s) == -4
+    assert L.moe_combine_bwd(h.ptr, p, 1, 64, None, p, p, p, s) == -1      # grad_w needs weights
+    assert L.moe_combine_bwd(h.ptr, p, 1, 64, p, None, p, p, s) == -1      # ... and y
+    assert L.moe_dispatch_bwd(h.ptr, p, 1, 64, p, None, p, p, s) == -1     # grad_s needs x
+    assert L.moe_dispatch(h.ptr, None, 1, 64, None, 0, p, None, s) == -1
+    assert h.check() == 0
+
+
+def test_bench_copy():
+    a = torch.randn(1 << 20, device=DEV)
+    b = torch.empty_like(a)
+    M.moe_bench_copy(b, a)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
