@@ -67,7 +67,7 @@ __all__ = [
 ]
 
 # Canonical reduction geometry for the router-weight gradients (see
-# ``canonical_dot``): 16-byte chunks spread over 64 partial sums.
+# ``canonical_dot``): 16-byte chunks, grouped into segments of 64 chunks.
 CHUNK_BYTES = 16
 LANES = 64
 
@@ -342,15 +342,19 @@ def canonical_dot(a: np.ndarray, b: np.ndarray, dtype: str) -> np.ndarray:
     The pages fix float32 accumulation but not the order of a length-H sum,
     and at these magnitudes (|dot| ~ sqrt(H)) a different order moves the
     result by whole float32 ulps.  The order is therefore part of the
-    contract:
+    contract (segment-major, so that one row can be spread over several
+    64-lane wavefronts that each own one segment):
 
     1. Cut each row into 16-byte chunks of V elements (V = 4 for f32, 8 for
-       bf16), NV = H / V chunks.  Chunk j belongs to partial sum l = j mod 64.
-    2. Each of the 64 partial sums starts at +0.0 and adds, for its chunks in
-       increasing j and inside a chunk in increasing element order, the
-       float32 product a*b (product rounded, then sum rounded).
-    3. The 64 partials are folded pairwise: for s = 32, 16, 8, 4, 2, 1 every
-       partial l becomes L[l] + L[l xor s].  The result is partial 0.
+       bf16), NV = H / V chunks, and the chunks into segments of 64
+       consecutive chunks (the last segment is padded with +0.0 chunks).
+    2. Each chunk's partial starts at +0.0 and adds its V float32 products
+       a*b in element order (product rounded, then sum rounded).
+    3. Each segment folds its 64 chunk partials pairwise: for s = 32, 16, 8,
+       4, 2, 1 partial l becomes L[l] + L[l xor s]; the segment's value is
+       partial 0.
+    4. The result starts at +0.0 and adds the segment values in segment
+       order.
     """
     a = np.asarray(a)
     b = np.asarray(b)
@@ -359,13 +363,17 @@ def canonical_dot(a: np.ndarray, b: np.ndarray, dtype: str) -> np.ndarray:
     if H % V:
         raise ValueError("H must be a whole number of 16-byte chunks")
     NV = H // V
+    NS = -(-NV // LANES)                                   # segments
     prod = (to_f32(a, dtype) * to_f32(b, dtype)).reshape(n, NV, V)   # float32 products
-    L = np.zeros((n, LANES), dtype=np.float32)
-    for j0 in range(0, NV, LANES):
-        width = min(LANES, NV - j0)          # partial sums that own a chunk in this round
-        for i in range(V):
-            L[:, :width] = L[:, :width] + prod[:, j0:j0 + width, i]
+    c = np.zeros((n, NS * LANES), dtype=np.float32)        # chunk partials, padded
+    for i in range(V):
+        c[:, :NV] = c[:, :NV] + prod[:, :, i]
+    c = c.reshape(n, NS, LANES)
     lane = np.arange(LANES)
     for s in (32, 16, 8, 4, 2, 1):
-        L = L + L[:, lane ^ s]
-    return L[:, 0].copy()
+        c = c + c[:, :, lane ^ s]
+    seg = c[:, :, 0]
+    out = np.zeros(n, dtype=np.float32)
+    for k in range(NS):
+        out = out + seg[:, k]
+    return out

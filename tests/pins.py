@@ -301,37 +301,45 @@ def check_dot_bound(dot_fn, dtype, n=5, H=2048, seed=1):
 def dot_order_cases(dtype="f32"):
     """Crafted rows whose canonical result is derived by hand.
 
-    Rows have 256 chunks of V elements (V = 4 for f32, 8 for bf16), so 64
-    partial sums own 4 chunks each.  ``at(j, i)`` is element i of chunk j.
-    b is all ones, so every product is the a value itself.
+    Rows have 256 chunks of V elements (V = 4 for f32, 8 for bf16), so 4
+    segments of 64 chunks.  ``at(j, i)`` is element i of chunk j.  b is all
+    ones, so every product is the a value itself.  All values are exact in
+    bf16.  Write B = 2^24: B + 1 is a float32 tie and rounds to B (even).
 
-    Case A: 2^24 at (0,0) and 1 at (0,1) -- both on partial 0 in its first
-    round -- then -2^24 at (64,0) -- partial 0, second round -- and 1 at
-    (1,0) on partial 1.  Partial 0: 2^24 + 1 ties to even -> 2^24, then
-    -2^24 -> 0.  The fold adds partial 1's 1.0: result 1.0.  Left-to-right
-    order gives 0.0; the exact sum is 2.0.
+    Case A (fold order inside a segment): B at (0,0), -B at (1,0), 1 at
+    (32,0) and 1 at (33,0), all in segment 0.  Fold s=32: partial 0 = B + 1
+    -> B, partial 1 = -B + 1 = -(B - 1) exactly; s=16..2 add zeros; s=1:
+    B - (B - 1) = 1.  Result 1.0.  Left to right gives B - B + 1 + 1 = 2.0;
+    folding neighbours first (s = 1, ..., 32) gives 0 + 2 = 2.0; segments of
+    32 chunks give 0 + 2 = 2.0.
 
-    Case B: 2^24 at (0,0) on partial 0, -2^24 at (1,0) on partial 1, 1 at
-    (32,0) on partial 32 and 1 at (33,0) on partial 33.  Fold s=32: partial
-    0 = 2^24 + 1 -> 2^24, partial 1 = -2^24 + 1 = -(2^24 - 1) exactly;
-    s=16..2 add zeros; s=1: 2^24 - (2^24 - 1) = 1.0.  Folding neighbours
-    first (s = 1, 2, ..., 32) would give 0 then 0 + 2 = 2.0.
+    Case B (segments are folded on their own, then added): B at (0,0) in
+    segment 0, 1 at (64,0) and 1 at (65,0) in segment 1.  Segment values B
+    and 2; result B + 2 exactly.  Carrying one partial per lane across
+    segments (chunks 0 and 64 on partial 0) absorbs each 1 into B: B.  Left
+    to right also gives B.
 
-    Case C: 2^24 at (0,0), 1 at (32,0) and 1 at (32,1).  With 64 partials,
-    partial 32 holds 2 exactly and the fold gives 2^24 + 2 exactly.  With 32
-    partials (or left to right) both ones would be absorbed one at a time:
-    2^24.
+    Case C (segment values added in sequence from +0.0): 1 at (0,0), B at
+    (64,0), 1 at (128,0), 1 at (192,0): segment values 1, B, 1, 1.
+    Sequentially: 1 + B -> B, + 1 -> B, + 1 -> B.  Result B.  A pairwise tree
+    gives (1 + B -> B) + (1 + 1) = B + 2; adding in reverse order gives
+    2 + B = B + 2, + 1 -> B + 4 (tie to even).
+
+    Case D (elements of a chunk are added in order): B at (0,0), 1 at (0,1)
+    and 1 at (0,2).  Chunk partial: B + 1 -> B, + 1 -> B.  Result B.  Adding
+    the chunk's elements last to first gives 1 + 1 + B = B + 2.
     """
     V = 4 if dtype == "f32" else 8
     H = 256 * V
-    a = np.zeros((3, H), np.float32)
-    b = np.ones((3, H), np.float32)
+    a = np.zeros((4, H), np.float32)
+    b = np.ones((4, H), np.float32)
     at = lambda j, i: j * V + i
     big = 2.0 ** 24
-    a[0, at(0, 0)], a[0, at(0, 1)], a[0, at(64, 0)], a[0, at(1, 0)] = big, 1.0, -big, 1.0
-    a[1, at(0, 0)], a[1, at(1, 0)], a[1, at(32, 0)], a[1, at(33, 0)] = big, -big, 1.0, 1.0
-    a[2, at(0, 0)], a[2, at(32, 0)], a[2, at(32, 1)] = big, 1.0, 1.0
-    expect = np.array([1.0, 1.0, big + 2.0], np.float32)
+    a[0, at(0, 0)], a[0, at(1, 0)], a[0, at(32, 0)], a[0, at(33, 0)] = big, -big, 1.0, 1.0
+    a[1, at(0, 0)], a[1, at(64, 0)], a[1, at(65, 0)] = big, 1.0, 1.0
+    a[2, at(0, 0)], a[2, at(64, 0)], a[2, at(128, 0)], a[2, at(192, 0)] = 1.0, big, 1.0, 1.0
+    a[3, at(0, 0)], a[3, at(0, 1)], a[3, at(0, 2)] = big, 1.0, 1.0
+    expect = np.array([1.0, big + 2.0, big, big], np.float32)
     if dtype == "bf16":
         a = (a.view(np.uint32) >> 16).astype(np.uint16)
         b = (b.view(np.uint32) >> 16).astype(np.uint16)

@@ -114,24 +114,45 @@ def dot_sequential(a, b, dtype):
     return acc
 
 
-def dot_32_lanes(a, b, dtype):
-    # the canonical algorithm with 32 partial sums instead of 64
+def _chunk_partials(a, b, dtype, width, reverse_elems=False):
+    """Chunk partials padded to segments of ``width`` chunks: [n, NS, width]."""
     V = O.CHUNK_BYTES // (4 if dtype == "f32" else 2)
     n, Hh = np.asarray(a).shape
     NV = Hh // V
+    NS = -(-NV // width)
     prod = (O.to_f32(a, dtype) * O.to_f32(b, dtype)).reshape(n, NV, V)
-    L = np.zeros((n, 32), np.float32)
-    for j0 in range(0, NV, 32):
-        width = min(32, NV - j0)
-        for i in range(V):
-            L[:, :width] = L[:, :width] + prod[:, j0:j0 + width, i]
-    lane = np.arange(32)
-    for s in (16, 8, 4, 2, 1):
-        L = L + L[:, lane ^ s]
-    return L[:, 0].copy()
+    c = np.zeros((n, NS * width), np.float32)
+    order = range(V - 1, -1, -1) if reverse_elems else range(V)
+    for i in order:
+        c[:, :NV] = c[:, :NV] + prod[:, :, i]
+    return c.reshape(n, NS, width)
+
+
+def _fold(c, steps):
+    lane = np.arange(c.shape[-1])
+    for s in steps:
+        c = c + c[..., lane ^ s]
+    return c[..., 0]
+
+
+def _seq(seg):
+    out = np.zeros(seg.shape[0], np.float32)
+    for k in range(seg.shape[1]):
+        out = out + seg[:, k]
+    return out
+
+
+def dot_32_lanes(a, b, dtype):
+    # the canonical algorithm with segments of 32 chunks
+    return _seq(_fold(_chunk_partials(a, b, dtype, 32), (16, 8, 4, 2, 1)))
 
 
 def dot_fold_reversed(a, b, dtype):
+    return _seq(_fold(_chunk_partials(a, b, dtype, 64), (1, 2, 4, 8, 16, 32)))
+
+
+def dot_lane_carry(a, b, dtype):
+    # one partial per lane carried across segments, folded once at the end
     V = O.CHUNK_BYTES // (4 if dtype == "f32" else 2)
     n, Hh = np.asarray(a).shape
     NV = Hh // V
@@ -141,10 +162,21 @@ def dot_fold_reversed(a, b, dtype):
         width = min(64, NV - j0)
         for i in range(V):
             L[:, :width] = L[:, :width] + prod[:, j0:j0 + width, i]
-    lane = np.arange(64)
-    for s in (1, 2, 4, 8, 16, 32):
-        L = L + L[:, lane ^ s]
-    return L[:, 0].copy()
+    return _fold(L, (32, 16, 8, 4, 2, 1))
+
+
+def dot_segment_tree(a, b, dtype):
+    # segment values combined pairwise instead of in sequence
+    seg = _fold(_chunk_partials(a, b, dtype, 64), (32, 16, 8, 4, 2, 1))
+    while seg.shape[1] > 1:
+        if seg.shape[1] % 2:
+            seg = np.concatenate([seg, np.zeros((seg.shape[0], 1), np.float32)], axis=1)
+        seg = seg[:, 0::2] + seg[:, 1::2]
+    return seg[:, 0]
+
+
+def dot_chunk_reversed(a, b, dtype):
+    return _seq(_fold(_chunk_partials(a, b, dtype, 64, reverse_elems=True), (32, 16, 8, 4, 2, 1)))
 
 
 def bf16_truncate(x):
@@ -198,7 +230,8 @@ def test_layout_faults_fail_brute_force_and_invariants(mutant):
         pins.check_layout_invariants(mutant(idx, E, P), idx)
 
 
-@pytest.mark.parametrize("mutant", [dot_sequential, dot_32_lanes, dot_fold_reversed])
+@pytest.mark.parametrize("mutant", [dot_sequential, dot_32_lanes, dot_fold_reversed, dot_lane_carry,
+                                    dot_segment_tree, dot_chunk_reversed])
 def test_dot_order_faults_fail_hand_derived_cases(mutant):
     for dtype in ("f32", "bf16"):
         with pytest.raises(AssertionError):
