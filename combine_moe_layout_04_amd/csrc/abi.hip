@@ -86,8 +86,15 @@ int check_rows(const moe_handle_s* h, int dtype, int64_t H, int* NV) {
   if (H < 1 || (H * eb) % 16 != 0) return MOE_ERR_SHAPE;
   const int64_t nv = H * eb / 16;
   if (nv >= (int64_t(1) << 31) || nv * h->T * h->K >= (int64_t(1) << 62)) return MOE_ERR_UNSUPPORTED;
+  // one wave per (token, segment): the grid must fit in a 32-bit wave index
+  if (moe::row_waves(h->T, (int)nv, 1) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   *NV = (int)nv;
   return MOE_OK;
+}
+
+// The router-weight-gradient kernels keep one float per (segment, k) in LDS.
+int check_dot(const moe_handle_s* h, int NV) {
+  return moe::dot_lds_bytes(NV, h->K) <= moe::kMaxDotLds ? MOE_OK : MOE_ERR_UNSUPPORTED;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -111,7 +118,7 @@ int moe_workspace_size(int64_t T, int K, int E, int P, size_t* bytes) {
 
 int moe_handle_create(moe_handle_t* out, const moe_tuning* tuning) {
   if (!out) return MOE_ERR_INVALID_ARG;
-  moe::Tuning t{4, 1, 4};  // defaults: 4 chunks/lane (scatter), receive-row NT stores, 4 waves/WG
+  moe::Tuning t{1, 1, 4};  // defaults: one segment per wave, non-temporal receive rows, 4 waves/WG
   if (tuning) {
     const int c = tuning->chunks_per_lane, n = tuning->nontemporal, w = tuning->waves_per_block;
     if (!(c == 0 || c == 1 || c == 2 || c == 4)) return MOE_ERR_INVALID_ARG;
@@ -232,31 +239,29 @@ int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H, const float
   a.R = (int)(h->T * h->K);
   a.dtype = dtype;
   a.status = ws_ptr<int>(h, h->plan.status);
-  moe::Tuning t = h->tune;
-  t.chunks_per_lane = t.chunks_per_lane >= 4 ? 2 : t.chunks_per_lane;  // gather keeps K rows live
-  return hip_status(moe::launch_gather(a, t, stream));
+  return hip_status(moe::launch_gather(a, h->tune, stream));
 }
 
 int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
                     const float* topk_weights, const void* y, void* grad_y, float* grad_w,
                     hipStream_t stream) {
   int NV = 0;
-  const int st = check_rows(h, dtype, H, &NV);
+  int st = check_rows(h, dtype, H, &NV);
   if (st != MOE_OK) return st;
   if (grad_w && (!topk_weights || !y)) return MOE_ERR_INVALID_ARG;
+  if (grad_w && (st = check_dot(h, NV)) != MOE_OK) return st;
   if (h->T == 0) return MOE_OK;
   if (!grad_out || !grad_y) return MOE_ERR_INVALID_ARG;
   if (!aligned(grad_out, 16) || !aligned(grad_y, 16) || (grad_w && !aligned(y, 16)))
     return MOE_ERR_ALIGNMENT;
   if ((topk_weights && !aligned(topk_weights, 4)) || (grad_w && !aligned(grad_w, 4)))
     return MOE_ERR_ALIGNMENT;
+  // rows: a dispatch of the output gradient, scaled by the weights
   moe::ScatterArgs a{};
   a.src = grad_out;
   a.recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
   a.w = topk_weights;
   a.dst = grad_y;
-  a.other = grad_w ? y : nullptr;
-  a.dot_out = grad_w;
   a.T = (int)h->T;
   a.K = h->K;
   a.NV = NV;
@@ -264,40 +269,70 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   a.dtype = dtype;
   a.scale = topk_weights != nullptr;
   a.status = ws_ptr<int>(h, h->plan.status);
-  moe::Tuning t = h->tune;
-  if (grad_w && t.chunks_per_lane >= 4) t.chunks_per_lane = 2;  // dot keeps K rows live
-  return hip_status(moe::launch_scatter(a, t, stream));
+  st = hip_status(moe::launch_scatter(a, h->tune, stream));
+  if (st != MOE_OK || !grad_w) return st;
+  // router-weight gradient: a separate pass over grad_out and y (measured
+  // faster than fusing it into the row stores: HBM turns around less)
+  moe::DotArgs d{};
+  d.tok = grad_out;
+  d.rcv = y;
+  d.recv_pos = a.recv_pos;
+  d.w = topk_weights;
+  d.dot_out = grad_w;
+  d.T = a.T;
+  d.K = a.K;
+  d.NV = NV;
+  d.R = a.R;
+  d.dtype = dtype;
+  d.gather = false;
+  d.status = a.status;
+  return hip_status(moe::launch_token_dot(d, h->tune, stream));
 }
 
 int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H,
                      const float* topk_weights, const void* x, void* grad_x, float* grad_s,
                      hipStream_t stream) {
   int NV = 0;
-  const int st = check_rows(h, dtype, H, &NV);
+  int st = check_rows(h, dtype, H, &NV);
   if (st != MOE_OK) return st;
   if (grad_s && (!topk_weights || !x)) return MOE_ERR_INVALID_ARG;
+  if (grad_s && (st = check_dot(h, NV)) != MOE_OK) return st;
   if (h->T == 0) return MOE_OK;
   if (!grad_recv || !grad_x) return MOE_ERR_INVALID_ARG;
   if (!aligned(grad_recv, 16) || !aligned(grad_x, 16) || (grad_s && !aligned(x, 16)))
     return MOE_ERR_ALIGNMENT;
   if ((topk_weights && !aligned(topk_weights, 4)) || (grad_s && !aligned(grad_s, 4)))
     return MOE_ERR_ALIGNMENT;
+  if (grad_s) {
+    // each receive row is read once for both the weighted sum and the dot
+    moe::DotArgs d{};
+    d.tok = x;
+    d.rcv = grad_recv;
+    d.recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
+    d.w = topk_weights;
+    d.dst = grad_x;
+    d.dot_out = grad_s;
+    d.T = (int)h->T;
+    d.K = h->K;
+    d.NV = NV;
+    d.R = (int)(h->T * h->K);
+    d.dtype = dtype;
+    d.gather = true;
+    d.status = ws_ptr<int>(h, h->plan.status);
+    return hip_status(moe::launch_token_dot(d, h->tune, stream));
+  }
   moe::GatherArgs a{};
   a.src = grad_recv;
   a.recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
   a.w = topk_weights;
   a.dst = grad_x;
-  a.other = grad_s ? x : nullptr;
-  a.dot_out = grad_s;
   a.T = (int)h->T;
   a.K = h->K;
   a.NV = NV;
   a.R = (int)(h->T * h->K);
   a.dtype = dtype;
   a.status = ws_ptr<int>(h, h->plan.status);
-  moe::Tuning t = h->tune;
-  t.chunks_per_lane = t.chunks_per_lane >= 4 ? 2 : t.chunks_per_lane;
-  return hip_status(moe::launch_gather(a, t, stream));
+  return hip_status(moe::launch_gather(a, h->tune, stream));
 }
 
 int moe_handle_field(moe_handle_t h, int field, void** dev_ptr, size_t* bytes) {

@@ -40,42 +40,62 @@ struct LayoutArgs {
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 
-// Token-row -> receive-row direction (dispatch, combine backward).
+// Token-row -> receive-row direction (dispatch, rows of the combine backward).
 struct ScatterArgs {
   const void* src;        // [T, NV] chunks
   const int* recv_pos;    // [T, K]
   const float* w;         // [T, K] or null
   void* dst;              // [R, NV] chunks
   float* scores_out;      // [R] or null
-  const void* other;      // [R, NV] chunks (dot operand) or null
-  float* dot_out;         // [T, K] or null
   int T, K, NV, R;
+  int ngrp;               // wave groups per token (set by the launcher)
   int dtype;
   bool scale;             // dst = round(w * src)
   int* status;
 };
 
-// Receive-row -> token-row direction (combine, dispatch backward).
+// Receive-row -> token-row direction (combine, unscaled dispatch backward).
 struct GatherArgs {
   const void* src;        // [R, NV] chunks
   const int* recv_pos;    // [T, K]
   const float* w;         // [T, K] or null (plain sum)
   void* dst;              // [T, NV] chunks
-  const void* other;      // [T, NV] chunks (dot operand) or null
-  float* dot_out;         // [T, K] or null
   int T, K, NV, R;
+  int ngrp;               // wave groups per token (set by the launcher)
   int dtype;
   int* status;
 };
 
+// Router-weight gradient dot[t,k] = <tok[t], rcv[recv_pos[t,k]]>, one
+// workgroup per token; with `gather` it also writes dst[t] = sum_k [w *] rcv.
+struct DotArgs {
+  const void* tok;        // [T, NV] chunks
+  const void* rcv;        // [R, NV] chunks
+  const int* recv_pos;    // [T, K]
+  const float* w;         // [T, K] or null
+  void* dst;              // [T, NV] chunks (gather only)
+  float* dot_out;         // [T, K]
+  int T, K, NV, R;
+  int dtype;
+  bool gather;
+  int* status;
+};
+
 struct Tuning {
-  int chunks_per_lane;  // 1, 2, 4
+  int chunks_per_lane;  // 1, 2, 4: consecutive 64-chunk segments per wave
   int nontemporal;      // 0, 1, 2
   int waves_per_block;  // 1, 2, 4, 8
 };
 
+constexpr int kMaxDotWaves = 16;         // waves of one token-dot workgroup
+constexpr size_t kMaxDotLds = 64 * 1024;  // LDS for its per-segment values
+
+size_t dot_lds_bytes(int NV, int K);
+int64_t row_waves(int64_t T, int NV, int cpl);
+
 hipError_t launch_scatter(const ScatterArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, const Tuning& t, hipStream_t s);
+hipError_t launch_token_dot(const DotArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 
 }  // namespace moe

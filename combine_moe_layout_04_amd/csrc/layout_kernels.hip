@@ -2,10 +2,12 @@
 // is_token_in_rank, prefix offsets, token send slots and stable receive
 // positions.  Two launches over the same token tiles:
 //
-//   count: per-tile expert histogram (LDS atomics: counts commute, so the
-//          result is deterministic), per-token partition bitmask,
-//          is_token_in_rank bytes, per-tile partition token counts;
-//   rank : global and per-tile prefix sums from the tile histograms, then a
+//   count: one thread per (t,k) pair: per-tile expert histogram (LDS
+//          atomics: counts commute, so the result is deterministic),
+//          per-token partition bitmask (LDS atomic OR), is_token_in_rank
+//          bytes, per-tile partition token counts;
+//   rank : global offsets and this tile's starts from one flat scan of the
+//          tile histograms (bucket-major, tile-minor), then a
 //          stable rank of every (t,k) pair among the pairs of its expert:
 //          wave64 ballots match equal expert ids, a popcount over the lanes
 //          below gives the rank inside 64 pairs, and per-(wave, expert)
@@ -46,20 +48,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// Exclusive scan of in[0..n) into out[0..n], out[n] = total, by one wave.
-__device__ void wave_exclusive_scan(const int* in, int* out, int n) {
-  const int lane = lane_id();
-  int carry = 0;
-  for (int base = 0; base < n; base += kWave) {
-    const int i = base + lane;
-    const int v = i < n ? in[i] : 0;
-    const int inc = wave_inclusive_scan(v);
-    if (i < n) out[i] = carry + inc - v;
-    carry += read_lane_i(inc, kWave - 1);
-  }
-  if (lane == 0) out[n] = carry;
-}
-
 size_t count_lds_bytes(int E, int P, int tile) {
   size_t ints = (size_t)(E + 1 + P);
   return ((ints * 4 + 7) & ~size_t(7)) + (size_t)tile * 8;
@@ -73,25 +61,31 @@ __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
       smem + ((size_t(a.E + 1 + a.P) * 4 + 7) & ~size_t(7)));  // [tile]
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  const int t0 = b * a.tile;
+  const int t1 = min(a.T, t0 + a.tile);
+  const int nt = max(0, t1 - t0);
   for (int i = tid; i < a.E + 1 + a.P; i += kLT) eh[i] = 0;
+  for (int i = tid; i < nt; i += kLT) msk[i] = 0ull;
   if (b == 0 && tid == 0) *a.status = 0;  // later kernels only OR bits in
   __syncthreads();
 
-  const int t0 = b * a.tile;
-  const int t1 = min(a.T, t0 + a.tile);
-  for (int t = t0 + tid; t < t1; t += kLT) {
-    unsigned long long m = 0;
-    for (int k = 0; k < a.K; ++k) {
-      const int e = load_expert(a.idx, a.itype, (int64_t)t * a.K + k, a.E);
-      atomicAdd(&eh[e], 1);
-      if (e < a.E) m |= 1ull << (e / a.epr);
-    }
-    msk[t - t0] = m;
-    a.tok_mask[t] = m;
-    unsigned long long mm = m;
-    while (mm) {
-      const int r = __ffsll((unsigned long long)mm) - 1;
-      mm &= mm - 1;
+  // one thread per (t,k) pair: coalesced id loads, LDS histogram and masks
+  const int np = nt * a.K;
+  const int64_t p0 = (int64_t)t0 * a.K;
+#pragma unroll 4
+  for (int i = tid; i < np; i += kLT) {
+    const int e = load_expert(a.idx, a.itype, p0 + i, a.E);
+    atomicAdd(&eh[e], 1);
+    if (e < a.E) atomicOr(&msk[i / a.K], 1ull << (e / a.epr));
+  }
+  __syncthreads();
+
+  for (int tt = tid; tt < nt; tt += kLT) {
+    unsigned long long m = msk[tt];
+    a.tok_mask[t0 + tt] = m;
+    while (m) {
+      const int r = __ffsll(m) - 1;
+      m &= m - 1;
       atomicAdd(&rh[r], 1);
     }
   }
@@ -99,7 +93,7 @@ __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
 
   for (int e = tid; e <= a.E; e += kLT) a.ehist[(size_t)e * a.nblk + b] = eh[e];
   for (int r = tid; r < a.P; r += kLT) a.rhist[(size_t)r * a.nblk + b] = rh[r];
-  const int nbytes = (t1 - t0) * a.P;
+  const int nbytes = nt * a.P;
   for (int i = tid; i < nbytes; i += kLT) {
     const int tt = i / a.P;
     const int r = i - tt * a.P;
@@ -107,65 +101,78 @@ __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
   }
 }
 
+// Exclusive scan, by the whole workgroup, of a [rows][nblk] histogram read
+// row-major (row = bucket, column = tile).  At (row, j) the scan is the
+// bucket's global start plus its count in the tiles before j.  Writes the
+// scan's column `b` to col_b[rows], its column 0 to col_0[rows] and the total
+// to col_0[rows].  Each thread scans a contiguous run (independent loads),
+// then the 256 run sums are scanned across the workgroup.
+__device__ void scan_histogram(const int* __restrict__ h, int rows, int nblk, int b, int* col_b,
+                               int* col_0, int* wsum) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int n = rows * nblk;
+  const int per = (n + kLT - 1) / kLT;
+  const int i0 = min(n, tid * per);
+  const int i1 = min(n, i0 + per);
+  int s = 0;
+#pragma unroll 8
+  for (int i = i0; i < i1; ++i) s += h[i];
+  const int inc = wave_inclusive_scan(s);
+  if (lane == kWave - 1) wsum[wv] = inc;
+  __syncthreads();
+  int run = inc - s;
+  for (int w = 0; w < wv; ++w) run += wsum[w];
+  int row = i0 / nblk;
+  int j = i0 - row * nblk;
+  for (int i = i0; i < i1; ++i) {
+    if (j == 0) col_0[row] = run;
+    if (j == b) col_b[row] = run;
+    run += h[i];
+    if (++j == nblk) {
+      j = 0;
+      ++row;
+    }
+  }
+  if (i0 < i1 && i1 == n) col_0[rows] = run;
+  __syncthreads();  // wsum is reused by the next scan
+}
+
 size_t rank_lds_ints(int E, int P) {
   const size_t E1 = (size_t)E + 1;
-  return E1 /*tot*/ + E1 /*pre*/ + (E1 + 1) /*off*/ + kLW * E1 /*cnt*/ + P /*rtot*/ +
-         P /*rpre*/ + (P + 1) /*soff*/ + (size_t)kWave * (P + 1) /*stage*/;
+  return E1 /*base*/ + (E1 + 1) /*off*/ + kLW * E1 /*cnt*/ + P /*rbase*/ + (P + 1) /*soff*/ +
+         kLW /*wsum*/ + (size_t)kWave * (P + 1) /*stage*/;
 }
 
 __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   extern __shared__ __align__(8) unsigned char smem[];
   const int E1 = a.E + 1;
-  int* tot = reinterpret_cast<int*>(smem);  // [E+1] pairs per bucket, all tiles
-  int* pre = tot + E1;                      // [E+1] pairs per bucket in earlier tiles
-  int* off = pre + E1;                      // [E+2] exclusive scan of tot
-  int* cnt = off + (E1 + 1);                // [kLW][E+1]
-  int* rtot = cnt + kLW * E1;               // [P]
-  int* rpre = rtot + a.P;                   // [P]
-  int* soff = rpre + a.P;                   // [P+1]
-  int* stage = soff + (a.P + 1);            // [64][P+1]
+  int* base = reinterpret_cast<int*>(smem);  // [E+1] first row of each bucket in this tile
+  int* off = base + E1;                      // [E+2] bucket offsets; off[E+1] = total
+  int* cnt = off + (E1 + 1);                 // [kLW][E+1]
+  int* rbase = cnt + kLW * E1;               // [P] this tile's first send row per partition
+  int* soff = rbase + a.P;                   // [P+1] send offsets
+  int* wsum = soff + (a.P + 1);              // [kLW]
+  int* stage = wsum + kLW;                   // [64][P+1]
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
 
-  // 1. totals and this tile's prefix, per bucket and per partition
-  for (int e = tid; e < E1; e += kLT) {
-    const int* row = a.ehist + (size_t)e * a.nblk;
-    int s = 0, p = 0;
-    for (int j = 0; j < a.nblk; ++j) {
-      if (j == b) p = s;
-      s += row[j];
-    }
-    tot[e] = s;
-    pre[e] = p;
-  }
-  for (int r = tid; r < a.P; r += kLT) {
-    const int* row = a.rhist + (size_t)r * a.nblk;
-    int s = 0, p = 0;
-    for (int j = 0; j < a.nblk; ++j) {
-      if (j == b) p = s;
-      s += row[j];
-    }
-    rtot[r] = s;
-    rpre[r] = p;
-  }
-  __syncthreads();
-
-  // 2. exclusive scans
-  if (wv == 0) wave_exclusive_scan(tot, off, E1);
-  if (wv == 1) wave_exclusive_scan(rtot, soff, a.P);
-  __syncthreads();
+  // 1-2. global offsets and this tile's starts, from the tile histograms
+  scan_histogram(a.ehist, E1, a.nblk, b, base, off, wsum);
+  scan_histogram(a.rhist, a.P, a.nblk, b, rbase, soff, wsum);
 
   // 3. global counts and offsets (tile 0 writes them)
   if (b == 0) {
-    for (int e = tid; e < a.E; e += kLT) a.num_tokens_per_expert[e] = tot[e];
+    for (int e = tid; e < a.E; e += kLT) a.num_tokens_per_expert[e] = off[e + 1] - off[e];
     for (int e = tid; e <= a.E; e += kLT) a.expert_offset[e] = off[e];
     for (int r = tid; r <= a.P; r += kLT) a.rank_offset[r] = off[r * a.epr];
-    for (int r = tid; r < a.P; r += kLT) a.num_tokens_per_rank[r] = rtot[r];
+    for (int r = tid; r < a.P; r += kLT) a.num_tokens_per_rank[r] = soff[r + 1] - soff[r];
     for (int r = tid; r <= a.P; r += kLT) a.send_offset[r] = soff[r];
-    if (tid == 0 && tot[a.E] != 0) atomicOr(a.status, MOE_STATUS_BAD_EXPERT);
+    if (tid == 0 && off[a.E + 1] != off[a.E]) atomicOr(a.status, MOE_STATUS_BAD_EXPERT);
   }
 
   // 4. per-wave bucket counts over contiguous pair ranges of this tile
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
 
   // 5. first receive row of each (wave, bucket)
   for (int e = tid; e < E1; e += kLT) {
-    int run = off[e] + pre[e];
+    int run = base[e];
     for (int w = 0; w < kLW; ++w) {
       const int c = cnt[w * E1 + e];
       cnt[w * E1 + e] = run;
@@ -235,9 +242,9 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
       for (int r = 0; r < a.P; ++r) {
         const int on = (int)((m >> r) & 1ull);
         const uint64_t bal = __ballot(on);
-        const int run = rpre[r];
-        stage[lane * (a.P + 1) + r] = on ? run + __popcll(bal & lanes_below(lane)) : -1;
-        if (lane == 0) rpre[r] = run + __popcll(bal);
+        const int run = rbase[r];
+        stage[lane * (a.P + 1) + r] = on ? run - soff[r] + __popcll(bal & lanes_below(lane)) : -1;
+        if (lane == 0) rbase[r] = run + __popcll(bal);
         __builtin_amdgcn_wave_barrier();
       }
       const int nt = min(kWave, t1 - c0);

@@ -1,21 +1,30 @@
 // Row movement between token order [T,H] and the expert-grouped receive
-// buffer [R,H], R = T*K.  One wave64 owns one token; its 64 lanes stride the
-// row in 16-byte chunks (lane l holds chunks l, l+64, l+128, ...), so every
-// wave-wide load or store touches 1 KiB of one row, fully coalesced.
+// buffer [R,H], R = T*K.
 //
-//   scatter (token -> receive rows): forward dispatch, and the backward of a
-//     combine.  The token row is read from HBM once and stored to each of
-//     its K receive rows (grouped by partition, since positions are
-//     expert-major); optional float32 scaling by w[t,k], optional per-row
-//     scores, optional dot <src[t], other[row]> (router-weight gradient).
-//   gather (receive rows -> token): forward combine, and the backward of a
-//     dispatch.  The K receive rows of a token are loaded together, reduced
-//     in float32 in k order from +0.0 (product and sum rounded separately),
-//     rounded once to the row type; optional dot <src[row], other[t]>.
+// A row is cut into 16-byte chunks and the chunks into segments of 64: one
+// wavefront-wide access is one segment, 1 KiB of one row, fully coalesced.
+// The unit of work is a (token, segment) pair, so a token's row is spread
+// over several wavefronts: many short-lived waves keep far more HBM requests
+// in flight than one wave walking a whole row.
 //
-// Dots keep one float32 partial per lane and fold the 64 partials with an
-// xor butterfly (s = 32..1): the fixed order documented in moe_layout.h.
-// Every receive-row index is bounds-checked against R before it is used.
+//   scatter (token -> receive rows): forward dispatch, and the row part of a
+//     combine's backward.  One wave loads its segment of the token row once
+//     and stores it to the K receive rows, optionally scaled by w[t,k] in
+//     float32 and rounded (scores absorbed before W2).  The receive rows are
+//     written once and not read back here, so their stores are non-temporal.
+//   gather (receive rows -> token): forward combine, and the backward of an
+//     unscaled dispatch.  One wave loads its segment of up to 8 receive rows
+//     at once (non-temporal: read once), sums them in float32 in k order from
+//     +0.0 (product and sum rounded separately) and rounds once.
+//   token dot (one workgroup per token, one wave per segment): the
+//     router-weight gradients <tok[t], rcv[recv_pos[t,k]]>, in the fixed
+//     order of moe_layout.h: per-chunk partials in element order, a butterfly
+//     fold per segment, then the segment values added in segment order
+//     through LDS.  Its gather variant also produces the weighted sum (the
+//     backward of a scaled dispatch reads each receive row once for both).
+//
+// Every receive-row index is bounds-checked against R before it is used; a
+// bad one raises MOE_STATUS_BAD_POSITION and the row is skipped.
 #include "device_common.h"
 #include "internal.h"
 #include "../../include/moe_layout.h"
@@ -23,246 +32,246 @@
 namespace moe {
 namespace {
 
-// Rows of one token are handled KG receive rows at a time (K <= 32 in any
-// number of groups); the dots are fused only when K <= KG (one group).
-constexpr int KG = 8;
+constexpr int KG = 8;  // receive rows in flight together per wave
 
-template <int DT, int CPL, bool SCALE, bool DOT, bool NT>
+template <bool NT>
+__device__ __forceinline__ u32x4 load_chunk(const u32x4* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+
+// The K receive rows and weights of token t: lane k < K holds pair (t,k).
+struct Pairs {
+  int pos = 0;
+  float w = 0.f;
+  bool bad = false;
+};
+
+__device__ __forceinline__ Pairs load_pairs(const int* recv_pos, const float* w, int t, int K, int R) {
+  Pairs q;
+  const int lane = lane_id();
+  if (lane < K) {
+    q.pos = recv_pos[(size_t)t * K + lane];
+    if (w) q.w = w[(size_t)t * K + lane];
+    q.bad = (unsigned)q.pos >= (unsigned)R;
+  }
+  return q;
+}
+
+// ---- scatter ----------------------------------------------------------------
+
+template <int DT, int CPL, bool SCALE, bool NT>
 __global__ __launch_bounds__(512) void scatter_kernel(ScatterArgs a) {
   constexpr int V = Elems<DT>::kPerChunk;
   const int lane = lane_id();
   const int wpb = blockDim.x / kWave;
-  const int t = blockIdx.x * wpb + (int)(threadIdx.x / kWave);
+  const int gw = blockIdx.x * wpb + (int)(threadIdx.x / kWave);
+  const int t = gw / a.ngrp;
   if (t >= a.T) return;  // wave-uniform
+  const int grp = gw - t * a.ngrp;
+  const int jb = grp * kWave * CPL + lane;  // this lane's first chunk
+
+  const Pairs q = load_pairs(a.recv_pos, a.w, t, a.K, a.R);
+  if (grp == 0) {
+    if (__ballot(q.bad) && lane == 0) atomicOr(a.status, MOE_STATUS_BAD_POSITION);
+    if (a.scores_out && lane < a.K && !q.bad) a.scores_out[q.pos] = q.w;
+  }
 
   const u32x4* src = static_cast<const u32x4*>(a.src) + (size_t)t * a.NV;
   u32x4* dst = static_cast<u32x4*>(a.dst);
-  const u32x4* oth = static_cast<const u32x4*>(a.other);
-
-  // lane k < K holds the receive row and weight of pair (t,k)
-  int mypos = 0;
-  float myw = 0.f;
-  bool bad = false;
-  if (lane < a.K) {
-    mypos = a.recv_pos[(size_t)t * a.K + lane];
-    if (a.w) myw = a.w[(size_t)t * a.K + lane];
-    bad = (unsigned)mypos >= (unsigned)a.R;
-  }
-  if (__ballot(bad) && lane == 0) atomicOr(a.status, MOE_STATUS_BAD_POSITION);
-  if (a.scores_out && lane < a.K && !bad) a.scores_out[mypos] = myw;
-
-  float L[DOT ? KG : 1];
+  u32x4 v[CPL];
 #pragma unroll
-  for (int k = 0; k < (DOT ? KG : 1); ++k) L[k] = 0.f;
-
-  for (int base = 0; base < a.NV; base += kWave * CPL) {
-    u32x4 v[CPL];
+  for (int c = 0; c < CPL; ++c) {
+    const int j = jb + c * kWave;
+    if (j < a.NV) v[c] = src[j];
+  }
+  float f[CPL][SCALE ? V : 1];
+  if constexpr (SCALE) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) unpack<DT>(v[c], f[c]);
+  }
+#pragma unroll 4
+  for (int k = 0; k < a.K; ++k) {
+    const int p = read_lane_i(q.pos, k);
+    if ((unsigned)p >= (unsigned)a.R) continue;  // uniform
+    u32x4* drow = dst + (size_t)p * a.NV;
+    const float s = read_lane_f(q.w, k);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int j = base + c * kWave + lane;
-      if (j < a.NV) v[c] = src[j];
-    }
-    for (int kg = 0; kg < a.K; kg += KG) {
-      // dot operands first, so no store sits between them and their use
-      u32x4 yv[DOT ? KG : 1][DOT ? CPL : 1];
-      if constexpr (DOT) {
+      const int j = jb + c * kWave;
+      if (j < a.NV) {
+        u32x4 o = v[c];
+        if constexpr (SCALE) {
+          float g[V];
 #pragma unroll
-        for (int kk = 0; kk < KG; ++kk) {
-          const int k = kg + kk;
-          if (k < a.K) {
-            const int p = read_lane_i(mypos, k);
-            if ((unsigned)p < (unsigned)a.R) {
-#pragma unroll
-              for (int c = 0; c < CPL; ++c) {
-                const int j = base + c * kWave + lane;
-                if (j < a.NV) yv[kk][c] = oth[(size_t)p * a.NV + j];
-              }
-            }
-          }
+          for (int i = 0; i < V; ++i) g[i] = __fmul_rn(s, f[c][i]);
+          o = pack<DT>(g);
         }
-      }
-#pragma unroll
-      for (int kk = 0; kk < KG; ++kk) {
-        const int k = kg + kk;
-        if (k < a.K) {
-          const int p = read_lane_i(mypos, k);
-          if ((unsigned)p < (unsigned)a.R) {
-            const float s = read_lane_f(myw, k);
-            u32x4* drow = dst + (size_t)p * a.NV;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-              const int j = base + c * kWave + lane;
-              if (j < a.NV) {
-                u32x4 o = v[c];
-                if constexpr (SCALE || DOT) {
-                  float f[V];
-                  unpack<DT>(v[c], f);
-                  if constexpr (DOT) {
-                    float g[V];
-                    unpack<DT>(yv[kk][c], g);
-#pragma unroll
-                    for (int i = 0; i < V; ++i) L[kk] = __fadd_rn(L[kk], __fmul_rn(f[i], g[i]));
-                  }
-                  if constexpr (SCALE) {
-#pragma unroll
-                    for (int i = 0; i < V; ++i) f[i] = __fmul_rn(s, f[i]);
-                    o = pack<DT>(f);
-                  }
-                }
-                store_chunk<NT>(drow + j, o);
-              }
-            }
-          }
-        }
-      }
-    }
-  }
-
-  if constexpr (DOT) {
-#pragma unroll
-    for (int k = 0; k < KG; ++k) {
-      if (k < a.K) {
-        const float d = fold64(L[k]);
-        if (lane == 0) a.dot_out[(size_t)t * a.K + k] = d;
+        store_chunk<NT>(drow + j, o);
       }
     }
   }
 }
 
-template <int DT, int CPL, bool WEIGHTED, bool DOT, bool NT>
+// ---- gather -----------------------------------------------------------------
+
+template <int DT, int CPL, bool WEIGHTED, bool NTL, bool NTS>
 __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a) {
   constexpr int V = Elems<DT>::kPerChunk;
   const int lane = lane_id();
   const int wpb = blockDim.x / kWave;
-  const int t = blockIdx.x * wpb + (int)(threadIdx.x / kWave);
+  const int gw = blockIdx.x * wpb + (int)(threadIdx.x / kWave);
+  const int t = gw / a.ngrp;
   if (t >= a.T) return;  // wave-uniform
+  const int grp = gw - t * a.ngrp;
+  const int jb = grp * kWave * CPL + lane;
+
+  const Pairs q = load_pairs(a.recv_pos, WEIGHTED ? a.w : nullptr, t, a.K, a.R);
+  if (grp == 0 && __ballot(q.bad) && lane == 0) atomicOr(a.status, MOE_STATUS_BAD_POSITION);
 
   const u32x4* src = static_cast<const u32x4*>(a.src);
-  u32x4* dst = static_cast<u32x4*>(a.dst) + (size_t)t * a.NV;
-  const u32x4* oth = static_cast<const u32x4*>(a.other) + (DOT ? (size_t)t * a.NV : 0);
+  float acc[CPL][V];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[c][i] = 0.f;
 
-  int mypos = 0;
-  float myw = 0.f;
-  bool bad = false;
-  if (lane < a.K) {
-    mypos = a.recv_pos[(size_t)t * a.K + lane];
-    if constexpr (WEIGHTED) myw = a.w[(size_t)t * a.K + lane];
-    bad = (unsigned)mypos >= (unsigned)a.R;
+  for (int kg = 0; kg < a.K; kg += KG) {
+    u32x4 yv[KG][CPL];
+    bool ok[KG];
+#pragma unroll
+    for (int kk = 0; kk < KG; ++kk) {
+      const int k = kg + kk;
+      ok[kk] = false;
+      if (k < a.K) {
+        const int p = read_lane_i(q.pos, k);
+        ok[kk] = (unsigned)p < (unsigned)a.R;
+        if (ok[kk]) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const int j = jb + c * kWave;
+            if (j < a.NV) yv[kk][c] = load_chunk<NTL>(src + (size_t)p * a.NV + j);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KG; ++kk) {
+      if (ok[kk]) {
+        const float s = read_lane_f(q.w, kg + kk);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int j = jb + c * kWave;
+          if (j < a.NV) {
+            float f[V];
+            unpack<DT>(yv[kk][c], f);
+            if constexpr (WEIGHTED) {
+#pragma unroll
+              for (int i = 0; i < V; ++i) acc[c][i] = __fadd_rn(acc[c][i], __fmul_rn(s, f[i]));
+            } else {
+#pragma unroll
+              for (int i = 0; i < V; ++i) acc[c][i] = __fadd_rn(acc[c][i], f[i]);
+            }
+          }
+        }
+      }
+    }
   }
-  if (__ballot(bad) && lane == 0) atomicOr(a.status, MOE_STATUS_BAD_POSITION);
+  u32x4* dst = static_cast<u32x4*>(a.dst) + (size_t)t * a.NV;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int j = jb + c * kWave;
+    if (j < a.NV) store_chunk<NTS>(dst + j, pack<DT>(acc[c]));
+  }
+}
 
-  float L[DOT ? KG : 1];
-#pragma unroll
-  for (int k = 0; k < (DOT ? KG : 1); ++k) L[k] = 0.f;
+// ---- token dot (router-weight gradients), optionally with the gather ---------
 
-  for (int base = 0; base < a.NV; base += kWave * CPL) {
-    float acc[CPL][V];
+template <int DT, bool GATHER, bool WEIGHTED, bool NTL, bool NTS>
+__global__ __launch_bounds__(1024) void token_dot_kernel(DotArgs a) {
+  constexpr int V = Elems<DT>::kPerChunk;
+  extern __shared__ float seg_val[];  // [nseg][K]
+  const int lane = lane_id();
+  const int wave = (int)(threadIdx.x / kWave);
+  const int nw = blockDim.x / kWave;
+  const int t = blockIdx.x;
+  const int nseg = (a.NV + kWave - 1) / kWave;
+
+  const Pairs q = load_pairs(a.recv_pos, a.w, t, a.K, a.R);
+  if (wave == 0 && __ballot(q.bad) && lane == 0) atomicOr(a.status, MOE_STATUS_BAD_POSITION);
+
+  const u32x4* tok = static_cast<const u32x4*>(a.tok) + (size_t)t * a.NV;
+  const u32x4* rcv = static_cast<const u32x4*>(a.rcv);
+
+  for (int sg = wave; sg < nseg; sg += nw) {  // wave-uniform
+    const int j = sg * kWave + lane;
+    const bool valid = j < a.NV;
+    float x[V];
+    if (valid) {
+      unpack<DT>(tok[j], x);
+    } else {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+      for (int i = 0; i < V; ++i) x[i] = 0.f;
+    }
+    float acc[GATHER ? V : 1];
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[c][i] = 0.f;
+    for (int i = 0; i < (GATHER ? V : 1); ++i) acc[i] = 0.f;
 
     for (int kg = 0; kg < a.K; kg += KG) {
-      // the group's rows all in flight before the first use
-      u32x4 yv[KG][CPL];
+      u32x4 yv[KG];
       bool ok[KG];
 #pragma unroll
       for (int kk = 0; kk < KG; ++kk) {
         const int k = kg + kk;
         ok[kk] = false;
         if (k < a.K) {
-          const int p = read_lane_i(mypos, k);
+          const int p = read_lane_i(q.pos, k);
           ok[kk] = (unsigned)p < (unsigned)a.R;
-          if (ok[kk]) {
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-              const int j = base + c * kWave + lane;
-              if (j < a.NV) yv[kk][c] = src[(size_t)p * a.NV + j];
-            }
-          }
-        }
-      }
-      u32x4 xv[DOT ? CPL : 1];
-      if constexpr (DOT) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int j = base + c * kWave + lane;
-          if (j < a.NV) xv[c] = oth[j];
+          if (ok[kk] && valid) yv[kk] = load_chunk<NTL>(rcv + (size_t)p * a.NV + j);
         }
       }
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int j = base + c * kWave + lane;
-        if (j < a.NV) {
-          float xf[DOT ? V : 1];
-          if constexpr (DOT) unpack<DT>(xv[c], xf);
+      for (int kk = 0; kk < KG; ++kk) {
+        const int k = kg + kk;
+        if (k < a.K) {  // uniform: every lane takes part in the fold
+          float c = 0.f;
+          if (ok[kk] && valid) {
+            float f[V];
+            unpack<DT>(yv[kk], f);
 #pragma unroll
-          for (int kk = 0; kk < KG; ++kk) {
-            if (ok[kk]) {
-              float f[V];
-              unpack<DT>(yv[kk][c], f);
-              if constexpr (DOT) {
-#pragma unroll
-                for (int i = 0; i < V; ++i) L[kk] = __fadd_rn(L[kk], __fmul_rn(f[i], xf[i]));
-              }
+            for (int i = 0; i < V; ++i) c = __fadd_rn(c, __fmul_rn(x[i], f[i]));
+            if constexpr (GATHER) {
               if constexpr (WEIGHTED) {
-                const float s = read_lane_f(myw, kg + kk);
+                const float s = read_lane_f(q.w, k);
 #pragma unroll
-                for (int i = 0; i < V; ++i) acc[c][i] = __fadd_rn(acc[c][i], __fmul_rn(s, f[i]));
+                for (int i = 0; i < V; ++i) acc[i] = __fadd_rn(acc[i], __fmul_rn(s, f[i]));
               } else {
 #pragma unroll
-                for (int i = 0; i < V; ++i) acc[c][i] = __fadd_rn(acc[c][i], f[i]);
+                for (int i = 0; i < V; ++i) acc[i] = __fadd_rn(acc[i], f[i]);
               }
             }
           }
+          c = fold64(c);
+          if (lane == 0) seg_val[sg * a.K + k] = c;
         }
       }
     }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int j = base + c * kWave + lane;
-      if (j < a.NV) store_chunk<NT>(dst + j, pack<DT>(acc[c]));
-    }
-  }
-
-  if constexpr (DOT) {
-#pragma unroll
-    for (int k = 0; k < KG; ++k) {
-      if (k < a.K) {
-        const float d = fold64(L[k]);
-        if (lane == 0) a.dot_out[(size_t)t * a.K + k] = d;
+    if constexpr (GATHER) {
+      if (valid) {
+        u32x4* dst = static_cast<u32x4*>(a.dst) + (size_t)t * a.NV;
+        store_chunk<NTS>(dst + j, pack<DT>(acc));
       }
     }
   }
-}
-
-// Router-weight gradient on its own, for K > KG: one wave per pair (t,k),
-// dot of token row t of `tok` and receive row recv_pos[t,k] of `rcv`, in the
-// same lane order and fold as the fused path.
-template <int DT>
-__global__ __launch_bounds__(256) void pair_dot_kernel(const u32x4* tok, const u32x4* rcv,
-                                                       const int* recv_pos, float* out,
-                                                       int T, int K, int NV, int R) {
-  constexpr int V = Elems<DT>::kPerChunk;
-  const int lane = lane_id();
-  const int64_t pair = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (pair >= (int64_t)T * K) return;  // wave-uniform
-  const int t = (int)(pair / K);
-  const int p = recv_pos[pair];
-  float L = 0.f;
-  if ((unsigned)p < (unsigned)R) {
-    const u32x4* ta = tok + (size_t)t * NV;
-    const u32x4* rb = rcv + (size_t)p * NV;
-    for (int j = lane; j < NV; j += kWave) {
-      float f[V], g[V];
-      unpack<DT>(ta[j], f);
-      unpack<DT>(rb[j], g);
-#pragma unroll
-      for (int i = 0; i < V; ++i) L = __fadd_rn(L, __fmul_rn(f[i], g[i]));
-    }
+  __syncthreads();
+  if ((int)threadIdx.x < a.K) {
+    float d = 0.f;
+    for (int sg = 0; sg < nseg; ++sg) d = __fadd_rn(d, seg_val[sg * a.K + threadIdx.x]);
+    a.dot_out[(size_t)t * a.K + threadIdx.x] = d;
   }
-  const float d = fold64(L);
-  if (lane == 0) out[pair] = d;
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst,
@@ -272,84 +281,94 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst,
   for (; i < n; i += stride) dst[i] = src[i];
 }
 
-// ---- template selection ---------------------------------------------------
+// ---- launch geometry and template selection -----------------------------------
 
-template <int DT, int CPL, bool SCALE, bool DOT, bool NT>
-hipError_t go_scatter(const ScatterArgs& a, int wpb, hipStream_t s) {
-  hipLaunchKernelGGL((scatter_kernel<DT, CPL, SCALE, DOT, NT>),
-                     dim3((a.T + wpb - 1) / wpb), dim3(wpb * kWave), 0, s, a);
+int groups_per_token(int NV, int cpl) { return (NV + kWave * cpl - 1) / (kWave * cpl); }
+
+template <int DT, int CPL, bool SCALE>
+hipError_t go_scatter(const ScatterArgs& a0, const Tuning& tu, hipStream_t s) {
+  ScatterArgs a = a0;
+  a.ngrp = groups_per_token(a.NV, CPL);
+  const int wpb = tu.waves_per_block;
+  const int64_t waves = (int64_t)a.T * a.ngrp;
+  const dim3 grid((unsigned)((waves + wpb - 1) / wpb)), block(wpb * kWave);
+  if (tu.nontemporal >= 1)
+    hipLaunchKernelGGL((scatter_kernel<DT, CPL, SCALE, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((scatter_kernel<DT, CPL, SCALE, false>), grid, block, 0, s, a);
   return hipGetLastError();
-}
-
-template <int DT, int CPL, bool SCALE, bool DOT>
-hipError_t sc_nt(const ScatterArgs& a, const Tuning& t, hipStream_t s) {
-  return t.nontemporal >= 1 ? go_scatter<DT, CPL, SCALE, DOT, true>(a, t.waves_per_block, s)
-                            : go_scatter<DT, CPL, SCALE, DOT, false>(a, t.waves_per_block, s);
 }
 
 template <int DT, int CPL>
 hipError_t sc_mode(const ScatterArgs& a, const Tuning& t, hipStream_t s) {
-  if (a.dot_out && a.K <= KG) return sc_nt<DT, CPL, true, true>(a, t, s);  // dot implies weights
-  if (a.scale) return sc_nt<DT, CPL, true, false>(a, t, s);
-  return sc_nt<DT, CPL, false, false>(a, t, s);
-}
-
-template <int DT>
-hipError_t pair_dot(const void* tok, const void* rcv, const int* pos, float* out, int T, int K,
-                    int NV, int R, hipStream_t s) {
-  const int64_t pairs = (int64_t)T * K;
-  const int wpb = 4;
-  hipLaunchKernelGGL((pair_dot_kernel<DT>), dim3((unsigned)((pairs + wpb - 1) / wpb)),
-                     dim3(wpb * kWave), 0, s, static_cast<const u32x4*>(tok),
-                     static_cast<const u32x4*>(rcv), pos, out, T, K, NV, R);
-  return hipGetLastError();
+  return a.scale ? go_scatter<DT, CPL, true>(a, t, s) : go_scatter<DT, CPL, false>(a, t, s);
 }
 
 template <int DT>
 hipError_t sc_cpl(const ScatterArgs& a, const Tuning& t, hipStream_t s) {
-  hipError_t e;
   switch (t.chunks_per_lane) {
-    case 1: e = sc_mode<DT, 1>(a, t, s); break;
-    case 2: e = sc_mode<DT, 2>(a, t, s); break;
-    default: e = sc_mode<DT, 4>(a, t, s); break;
+    case 2: return sc_mode<DT, 2>(a, t, s);
+    case 4: return sc_mode<DT, 4>(a, t, s);
+    default: return sc_mode<DT, 1>(a, t, s);
   }
-  if (e != hipSuccess || !a.dot_out || a.K <= KG) return e;
-  return pair_dot<DT>(a.src, a.other, a.recv_pos, a.dot_out, a.T, a.K, a.NV, a.R, s);
 }
 
-template <int DT, int CPL, bool W, bool DOT, bool NT>
-hipError_t go_gather(const GatherArgs& a, int wpb, hipStream_t s) {
-  hipLaunchKernelGGL((gather_kernel<DT, CPL, W, DOT, NT>),
-                     dim3((a.T + wpb - 1) / wpb), dim3(wpb * kWave), 0, s, a);
+template <int DT, int CPL, bool W>
+hipError_t go_gather(const GatherArgs& a0, const Tuning& tu, hipStream_t s) {
+  GatherArgs a = a0;
+  a.ngrp = groups_per_token(a.NV, CPL);
+  const int wpb = tu.waves_per_block;
+  const int64_t waves = (int64_t)a.T * a.ngrp;
+  const dim3 grid((unsigned)((waves + wpb - 1) / wpb)), block(wpb * kWave);
+  switch (tu.nontemporal) {
+    case 0: hipLaunchKernelGGL((gather_kernel<DT, CPL, W, false, false>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((gather_kernel<DT, CPL, W, true, false>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((gather_kernel<DT, CPL, W, true, true>), grid, block, 0, s, a); break;
+  }
   return hipGetLastError();
-}
-
-template <int DT, int CPL, bool W, bool DOT>
-hipError_t ga_nt(const GatherArgs& a, const Tuning& t, hipStream_t s) {
-  return t.nontemporal >= 2 ? go_gather<DT, CPL, W, DOT, true>(a, t.waves_per_block, s)
-                            : go_gather<DT, CPL, W, DOT, false>(a, t.waves_per_block, s);
 }
 
 template <int DT, int CPL>
 hipError_t ga_mode(const GatherArgs& a, const Tuning& t, hipStream_t s) {
-  if (a.dot_out && a.K <= KG) return ga_nt<DT, CPL, true, true>(a, t, s);  // dot implies weights
-  if (a.w) return ga_nt<DT, CPL, true, false>(a, t, s);
-  return ga_nt<DT, CPL, false, false>(a, t, s);
+  return a.w ? go_gather<DT, CPL, true>(a, t, s) : go_gather<DT, CPL, false>(a, t, s);
 }
 
 template <int DT>
 hipError_t ga_cpl(const GatherArgs& a, const Tuning& t, hipStream_t s) {
-  hipError_t e;
   switch (t.chunks_per_lane) {
-    case 1: e = ga_mode<DT, 1>(a, t, s); break;
-    case 4: e = ga_mode<DT, 4>(a, t, s); break;
-    default: e = ga_mode<DT, 2>(a, t, s); break;
+    case 2: return ga_mode<DT, 2>(a, t, s);
+    case 4: return ga_mode<DT, 4>(a, t, s);
+    default: return ga_mode<DT, 1>(a, t, s);
   }
-  if (e != hipSuccess || !a.dot_out || a.K <= KG) return e;
-  return pair_dot<DT>(a.other, a.src, a.recv_pos, a.dot_out, a.T, a.K, a.NV, a.R, s);
+}
+
+template <int DT, bool G, bool W>
+hipError_t go_dot(const DotArgs& a, const Tuning& tu, hipStream_t s) {
+  const int nseg = (a.NV + kWave - 1) / kWave;
+  const int nw = nseg < kMaxDotWaves ? nseg : kMaxDotWaves;
+  const size_t lds = (size_t)nseg * a.K * sizeof(float);
+  const dim3 grid((unsigned)a.T), block(nw * kWave);
+  switch (tu.nontemporal) {
+    case 0: hipLaunchKernelGGL((token_dot_kernel<DT, G, W, false, false>), grid, block, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((token_dot_kernel<DT, G, W, true, false>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((token_dot_kernel<DT, G, W, true, true>), grid, block, lds, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t dot_mode(const DotArgs& a, const Tuning& t, hipStream_t s) {
+  if (!a.gather) return go_dot<DT, false, false>(a, t, s);
+  return a.w ? go_dot<DT, true, true>(a, t, s) : go_dot<DT, true, false>(a, t, s);
 }
 
 }  // namespace
+
+size_t dot_lds_bytes(int NV, int K) {
+  return (size_t)((NV + kWave - 1) / kWave) * (size_t)K * sizeof(float);
+}
+
+int64_t row_waves(int64_t T, int NV, int cpl) { return T * groups_per_token(NV, cpl); }
 
 hipError_t launch_scatter(const ScatterArgs& a, const Tuning& t, hipStream_t s) {
   return a.dtype == kF32 ? sc_cpl<kF32>(a, t, s) : sc_cpl<kBF16>(a, t, s);
@@ -357,6 +376,10 @@ hipError_t launch_scatter(const ScatterArgs& a, const Tuning& t, hipStream_t s) 
 
 hipError_t launch_gather(const GatherArgs& a, const Tuning& t, hipStream_t s) {
   return a.dtype == kF32 ? ga_cpl<kF32>(a, t, s) : ga_cpl<kBF16>(a, t, s);
+}
+
+hipError_t launch_token_dot(const DotArgs& a, const Tuning& t, hipStream_t s) {
+  return a.dtype == kF32 ? dot_mode<kF32>(a, t, s) : dot_mode<kBF16>(a, t, s);
 }
 
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {

@@ -37,7 +37,7 @@
  *   - Floating-point contract: products and sums in IEEE float32, each
  *     rounded on its own (no fused multiply-add); sums over k run in k order
  *     from +0.0; bfloat16 results are rounded to nearest, ties to even.
- *     Router-weight gradients use a fixed 64-partial order (see
+ *     Router-weight gradients use a fixed segment-major order (see
  *     moe_combine_bwd), so results are bitwise reproducible.
  */
 #ifndef MOE_LAYOUT_H
@@ -89,12 +89,15 @@ enum moe_field {
   MOE_FIELD_STATUS                = 10 /* int32 [1]   device status bits                   */
 };
 
-/* Optional launch knobs; zero means "library default". */
+/* Optional launch knobs; zero means "library default".  A row is cut into
+ * 16-byte chunks and the chunks into segments of 64 (one wavefront access);
+ * the row kernels run one wavefront per (token, segment group).           */
 typedef struct moe_tuning {
-  int chunks_per_lane;  /* 16-byte chunks each lane keeps in flight per row: 0, 1, 2 or 4 */
-  int nontemporal;      /* 0: default stores; 1: receive-row stores marked non-temporal;
-                           2: all row stores marked non-temporal                          */
-  int waves_per_block;  /* tokens (one wave each) per workgroup: 0, 1, 2, 4, 8           */
+  int chunks_per_lane;  /* consecutive segments per wavefront, i.e. chunks of one row each
+                           lane keeps in flight: 0 (= 1), 1, 2 or 4                        */
+  int nontemporal;      /* 0: default loads/stores; 1 (default): receive-row loads and
+                           stores marked non-temporal; 2: token-row stores too          */
+  int waves_per_block;  /* wavefronts per workgroup of the row kernels: 0 (= 4), 1, 2, 4, 8 */
 } moe_tuning;
 
 typedef struct moe_handle_s* moe_handle_t;
@@ -164,9 +167,12 @@ int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H,
  *   grad_y[recv_pos[t,k]] = round(w[t,k] * grad_out[t])  (copy if no weights)
  *   grad_w[t,k] = <grad_out[t], y[recv_pos[t,k]]>        (if grad_w != NULL)
  * grad_w needs topk_weights and y.  The dot product is float32 in a fixed
- * order: row cut into 16-byte chunks, chunk j added (element by element,
- * product rounded then sum rounded) into partial j mod 64, the 64 partials
- * then folded L[l] += L[l xor s] for s = 32,16,8,4,2,1; result = partial 0.
+ * order: the row is cut into 16-byte chunks and the chunks into segments of
+ * 64; each chunk's partial adds its element products in order from +0.0
+ * (product rounded, then sum rounded); each segment folds its 64 partials
+ * L[l] += L[l xor s] for s = 32,16,8,4,2,1 (absent chunks are +0.0) and
+ * takes partial 0; the result adds the segment values in order from +0.0.
+ * Needs ceil(H*elem/1024) * K * 4 <= 65536 (else MOE_ERR_UNSUPPORTED).
  *   grad_out [T,H], y [R,H], grad_y [R,H] dtype; grad_w [T,K] float32.     */
 int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
                     const float* topk_weights, const void* y, void* grad_y,
@@ -177,7 +183,7 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
  *   grad_s[t,k] = <grad_recv[recv_pos[t,k]], x[t]>        (if grad_s != NULL)
  * Pass topk_weights iff the forward dispatch scaled its rows (the scaling is
  * differentiated straight through its rounding).  grad_s needs topk_weights
- * and x; same dot order as moe_combine_bwd.
+ * and x; same dot order and size limit as moe_combine_bwd.
  *   grad_recv [R,H], x [T,H], grad_x [T,H] dtype; grad_s [T,K] float32.   */
 int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H,
                      const float* topk_weights, const void* x, void* grad_x,

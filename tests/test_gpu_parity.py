@@ -209,6 +209,7 @@ RAGGED = [  # name, overrides
     ("qwen3_30b_a3b", dict(T=131, H=1032)),
     ("diffusion_gemma", dict(T=67, H=520)),
     ("deepseek_v3", dict(T=45, H=4104)),
+    ("deepseek_v3", dict(T=19, H=8712)),    # 18 segments: more than one per dot wave
 ]
 
 
