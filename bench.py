@@ -44,6 +44,11 @@ def parse():
     ap.add_argument("--chunks-per-lane", type=int, default=0)
     ap.add_argument("--nontemporal", type=int, default=1)
     ap.add_argument("--waves-per-block", type=int, default=0)
+    ap.add_argument("--events", choices=["all", "dominant", "none"], default="dominant",
+                    help="HIP events in the timed region: around every call, around the "
+                         "dominant kernel's call only, or none")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph (no per-call events)")
     return ap.parse_args()
 
 
@@ -180,10 +185,11 @@ def main():
     torch.cuda.synchronize()
 
     names = ["layout", "dispatch", "combine", "combine_bwd", "dispatch_bwd"]
+    DOMINANT = "combine"  # the longest single kernel (a K-row gather-reduce)
 
-    def step_call(s, ev=None):
+    def step_call(s, ev=None, only=None):
         def mark(i):
-            if ev is not None:
+            if ev is not None and (only is None or i in only):
                 ev[i].record()
         mark(0)
         h = M.moe_layout(s["idx"], cfg.E, cfg.P, handle=s["h"], workspace=s["ws"])
@@ -205,22 +211,49 @@ def main():
     for s in sets:
         assert s["h"].check() == 0
 
+    graphs = None
+    if args.graph:
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for s in sets:
+                step_call(s)  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_call(s)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % nsets].replay()
+        torch.cuda.synchronize()
+
     K = args.steps
+    d = names.index(DOMINANT)
+    only = None if args.events == "all" else ({d, d + 1} if args.events == "dominant" else set())
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step_call(sets[i % nsets], evs[i])
+        if graphs is not None:
+            graphs[i % nsets].replay()
+        else:
+            step_call(sets[i % nsets], evs[i], only)
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
+    host_us = (t_enq - t0) * 1e6 / K
 
-    per_kernel_ms = {n: [] for n in names}
-    for e in evs:
-        for j, n in enumerate(names):
-            per_kernel_ms[n].append(e[j].elapsed_time(e[j + 1]))
-    avg_us = {n: float(np.mean(v)) * 1e3 for n, v in per_kernel_ms.items()}
-    med_us = {n: float(np.median(v)) * 1e3 for n, v in per_kernel_ms.items()}
+    # per-call event times (only the calls bracketed in the timed region)
+    timed = [n for j, n in enumerate(names)
+             if graphs is None and (only is None or (j in only and j + 1 in only))]
+    avg_us = {n: float(np.mean([e[names.index(n)].elapsed_time(e[names.index(n) + 1]) for e in evs])) * 1e3
+              for n in timed}
+    med_us = {n: float(np.median([e[names.index(n)].elapsed_time(e[names.index(n) + 1]) for e in evs])) * 1e3
+              for n in timed}
 
     # the copy kernel of known size, untimed: calibrates the traffic counters
     cbuf = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
@@ -232,8 +265,9 @@ def main():
     rows, index = layer_bytes(cfg)
     step_bytes = sum(rows.values())
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dom = max((n for n in names if n != "layout"), key=lambda n: avg_us[n])
-    achieved = rows[dom] / (avg_us[dom] * 1e-6) / 1e9
+    dom = DOMINANT
+    dom_us = avg_us.get(dom)
+    achieved = None if dom_us is None else rows[dom] / (dom_us * 1e-6) / 1e9
     traffic = traffic_from_profiles(dom)
 
     line = {
@@ -256,14 +290,17 @@ def main():
             "bytes_per_step": step_bytes,
             "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
             "us_per_layer": round(ms_per_step * 1e3, 2),
-            "kernel_avg_us": {n: round(v, 2) for n, v in avg_us.items()},
-            "kernel_median_us": {n: round(v, 2) for n, v in med_us.items()},
-            "kernel_GBps": {n: round(rows[n] / (avg_us[n] * 1e-6) / 1e9, 1) for n in names if rows[n]},
+            "call_avg_us": {n: round(v, 2) for n, v in avg_us.items()},
+            "call_median_us": {n: round(v, 2) for n, v in med_us.items()},
+            "call_GBps": {n: round(rows[n] / (avg_us[n] * 1e-6) / 1e9, 1) for n in avg_us if rows[n]},
             "index_bytes_per_step": sum(index.values()),
+            "host_enqueue_us_per_step": round(host_us, 1),
+            "timing": ("hip graph replay" if graphs is not None else "eager launches") +
+                      f", events: {args.events if graphs is None else 'none'}",
             "tuning": {"chunks_per_lane": args.chunks_per_lane, "nontemporal": args.nontemporal,
                        "waves_per_block": args.waves_per_block},
         },
-        "roofline": {
+        "roofline": None if achieved is None else {
             "bound": "hbm",
             "kernel": dom,
             "achieved": round(achieved, 1),
@@ -272,7 +309,7 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": rows[dom],
-            "avg_launch_us": round(avg_us[dom], 2),
+            "avg_launch_us": round(dom_us, 2),
         },
         "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds),
     }

@@ -11,20 +11,20 @@ namespace moe {
 struct WsLayout {
   size_t status, num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
       expert_offset, rank_offset, send_offset, token_slot, recv_pos, recv_token,
-      recv_k, tok_mask, ehist, rhist;
+      recv_k, hist;
   size_t total;
-  int nblk;  // layout workgroups
-  int tile;  // tokens per layout workgroup
+  int nblk;  // layout workgroups (token tiles)
+  int tile;  // tokens per tile, a multiple of 64
 };
 
 WsLayout plan_workspace(int64_t T, int K, int E, int P);
 
+constexpr int kLayoutThreads = 512;  // threads per layout workgroup
+
 struct LayoutArgs {
   const void* idx;
   int itype, T, K, E, P, epr, nblk, tile;
-  int* ehist;             // [E+1][nblk], expert-major
-  int* rhist;             // [P][nblk], partition-major
-  unsigned long long* tok_mask;  // [T]
+  int* hist;              // [E+1+P][nblk]: bucket counts, then partition token counts
   int* num_tokens_per_expert;
   int* num_tokens_per_rank;
   uint8_t* is_token_in_rank;
@@ -37,6 +37,10 @@ struct LayoutArgs {
   int* recv_k;
   int* status;
 };
+
+// Dynamic LDS of the two layout kernels.
+size_t layout_count_lds(int E, int P, int tile);
+size_t layout_rank_lds(int E, int P, int tile, int K);
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 
