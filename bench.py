@@ -19,6 +19,7 @@ one GPU's share of the exchange).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -95,6 +96,50 @@ def traffic_from_profiles(kernel: str):
         return None  # kernels changed since the counters were taken
     k = d.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+class HipEvents:
+    """Timing-only HIP events on torch's current stream, created with
+    hipEventDisableSystemFence so that recording one does not write back and
+    invalidate the caches (a default event's system-scope fence adds about
+    3 us to the interval it brackets).  Uses the HIP runtime instance torch
+    and the library already share in this process."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        import torch
+
+        torch.cuda.init()
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        self.L = L = ctypes.CDLL(path)
+        L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if L.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+        self._ms = ctypes.c_float()
+        self._byref = ctypes.byref
+
+    def record(self, i, stream):
+        if self.L.hipEventRecord(self.ev[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i, j):
+        if self.L.hipEventElapsedTime(self._byref(self._ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return self._ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.L.hipEventDestroy(e)
+        self.ev = []
 
 
 def cpu_baseline(cfg, budget_s):
@@ -190,7 +235,7 @@ def main():
     def step_call(s, ev=None, only=None):
         def mark(i):
             if ev is not None and (only is None or i in only):
-                ev[i].record()
+                hev.record(ev + i, stream)
         mark(0)
         h = M.moe_layout(s["idx"], cfg.E, cfg.P, handle=s["h"], workspace=s["ws"])
         mark(1)
@@ -233,14 +278,15 @@ def main():
     K = args.steps
     d = names.index(DOMINANT)
     only = None if args.events == "all" else ({d, d + 1} if args.events == "dominant" else set())
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hev = HipEvents(6 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         if graphs is not None:
             graphs[i % nsets].replay()
         else:
-            step_call(sets[i % nsets], evs[i], only)
+            step_call(sets[i % nsets], 6 * i, only)
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -250,10 +296,11 @@ def main():
     # per-call event times (only the calls bracketed in the timed region)
     timed = [n for j, n in enumerate(names)
              if graphs is None and (only is None or (j in only and j + 1 in only))]
-    avg_us = {n: float(np.mean([e[names.index(n)].elapsed_time(e[names.index(n) + 1]) for e in evs])) * 1e3
-              for n in timed}
-    med_us = {n: float(np.median([e[names.index(n)].elapsed_time(e[names.index(n) + 1]) for e in evs])) * 1e3
-              for n in timed}
+    call_ms = {n: [hev.elapsed_ms(6 * i + names.index(n), 6 * i + names.index(n) + 1) for i in range(K)]
+               for n in timed}
+    hev.close()
+    avg_us = {n: float(np.mean(v)) * 1e3 for n, v in call_ms.items()}
+    med_us = {n: float(np.median(v)) * 1e3 for n, v in call_ms.items()}
 
     # the copy kernel of known size, untimed: calibrates the traffic counters
     cbuf = torch.empty(1 << 28, dtype=torch.uint8, device=dev)

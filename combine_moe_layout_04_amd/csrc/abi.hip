@@ -23,23 +23,21 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 WsLayout plan_workspace(int64_t T, int K, int E, int P) {
   WsLayout w{};
-  // Token tiles of the layout.  A tile should hold about 4096 (t,k) pairs
-  // (few workgroups, short dependency chain) and the grid at most ~64 tiles
-  // (the rank kernel scans every tile's histogram); it is capped by the LDS
-  // the rank kernel needs to stage the tile's ids (2 bytes per pair, within
-  // 64 KiB together with its other arrays) and by the count kernel's per-
+  // Token tiles of the layout: at most 512 (t,k) pairs per tile (one per
+  // thread of a layout workgroup), unless that needs more than 128 tiles;
+  // then ~128 tiles, each wave of a tile looping over rounds of 64 pairs.
+  // Capped by the LDS the rank kernel stages the tile's ids in (2 bytes per
+  // pair, within 64 KiB with its other arrays) and the count kernel's per-
   // token masks (8 bytes per token).
   const int64_t fixed = (int64_t)layout_rank_lds(E, P, 0, K);
   int64_t pair_cap = (65536 - fixed) / 2;
   if (pair_cap > 16384) pair_cap = 16384;
-  int64_t tile_max = (pair_cap / K) & ~int64_t(63);
+  int64_t tile_max = pair_cap / K;
   if (tile_max > 4096) tile_max = 4096;
-  if (tile_max < 64) tile_max = 64;
-  int64_t tile_min = (4096 / K) & ~int64_t(63);
-  if (tile_min < 64) tile_min = 64;
-  if (tile_min > tile_max) tile_min = tile_max;
-  int64_t tile = (((T + 63) / 64) + 63) & ~int64_t(63);
-  if (tile < tile_min) tile = tile_min;
+  if (tile_max < 1) tile_max = 1;
+  int64_t tile = kLayoutThreads / K;
+  if (tile < 1) tile = 1;
+  if ((T + tile - 1) / tile > 128) tile = (T + 127) / 128;
   if (tile > tile_max) tile = tile_max;
   int64_t nblk = (T + tile - 1) / tile;
   if (nblk < 1) nblk = 1;
@@ -63,6 +61,7 @@ WsLayout plan_workspace(int64_t T, int K, int E, int P) {
   w.recv_pos = take((size_t)R * 4);
   w.recv_token = take((size_t)R * 4);
   w.recv_k = take((size_t)R * 4);
+  w.tok_mask = take((size_t)T * 8);
   w.hist = take((size_t)(E + 1 + P) * nblk * 4);
   w.total = o;
   return w;
@@ -184,6 +183,7 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
   a.nblk = plan.nblk;
   a.tile = plan.tile;
   a.hist = ws_ptr<int>(h, plan.hist);
+  a.tok_mask = ws_ptr<unsigned long long>(h, plan.tok_mask);
   a.num_tokens_per_expert = ws_ptr<int>(h, plan.num_tokens_per_expert);
   a.num_tokens_per_rank = ws_ptr<int>(h, plan.num_tokens_per_rank);
   a.is_token_in_rank = ws_ptr<uint8_t>(h, plan.is_token_in_rank);

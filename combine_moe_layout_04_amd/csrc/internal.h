@@ -11,10 +11,10 @@ namespace moe {
 struct WsLayout {
   size_t status, num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
       expert_offset, rank_offset, send_offset, token_slot, recv_pos, recv_token,
-      recv_k, hist;
+      recv_k, tok_mask, hist;
   size_t total;
   int nblk;  // layout workgroups (token tiles)
-  int tile;  // tokens per tile, a multiple of 64
+  int tile;  // tokens per tile
 };
 
 WsLayout plan_workspace(int64_t T, int K, int E, int P);
@@ -24,7 +24,8 @@ constexpr int kLayoutThreads = 512;  // threads per layout workgroup
 struct LayoutArgs {
   const void* idx;
   int itype, T, K, E, P, epr, nblk, tile;
-  int* hist;              // [E+1+P][nblk]: bucket counts, then partition token counts
+  int* hist;              // [nblk][E+1+P]: per tile, bucket counts then partition token counts
+  unsigned long long* tok_mask;  // [T] partitions each token is sent to
   int* num_tokens_per_expert;
   int* num_tokens_per_rank;
   uint8_t* is_token_in_rank;

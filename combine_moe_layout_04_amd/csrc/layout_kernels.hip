@@ -1,24 +1,28 @@
 // Layout of one routing decision: per-expert and per-partition counts,
 // is_token_in_rank, prefix offsets, token send slots and stable receive
-// positions.  Two launches over the same token tiles (a tile holds up to a
-// few thousand (t,k) pairs, so a layer needs only a handful of workgroups and
-// the path is a short chain of memory round trips):
+// positions.  Two launches over the same token tiles; a tile holds at most
+// 512 (t,k) pairs, one per thread of a 512-thread workgroup, so each wave
+// ranks one round of 64 pairs and a layer spreads over many CUs (beyond 128
+// tiles, for very large T, a tile holds more pairs and each wave loops):
 //
 //   count: one thread per (t,k) pair: per-tile expert histogram (LDS
 //          atomics: counts commute, so the result is deterministic),
 //          per-token partition bitmask (LDS atomic OR), is_token_in_rank,
-//          per-tile partition token counts.  The two histograms go to one
-//          [E+1+P][tiles] array, bucket-major.
-//   rank : one flat exclusive scan of that array gives every global offset
-//          and this tile's starts (each thread scans a run of it held in
-//          registers).  The tile's ids are staged in LDS; each wave ranks a
-//          contiguous span of pairs: wave64 ballots match equal ids, a
-//          popcount over the lanes below gives the rank inside 64 pairs, and
-//          per-(wave, expert) running counters in LDS carry it across rounds.
-//          Token send slots come from per-partition ballots over the tile's
-//          tokens.  No position is ever taken from an atomic, so the result
-//          depends on the routing alone (an activation-checkpoint replay of
-//          the same routing reproduces it bit for bit).
+//          per-tile partition token counts.  Each tile writes one contiguous
+//          row of a [tiles][E+1+P] histogram, and its tokens' masks.
+//   rank : every histogram column's total and its count in the tiles before
+//          this one (one thread per (column, tile range), all its loads in
+//          flight), then one workgroup scan over the columns: every global
+//          offset and this tile's starts.  Token send slots come from
+//          per-partition ballots over the tile's tokens.  The tile's ids are
+//          staged in LDS; each wave ranks a contiguous span of pairs: wave64
+//          ballots match equal ids, a popcount over the lanes below gives
+//          the rank inside 64 pairs, and per-(wave, expert) cursors in LDS
+//          carry it across waves (and rounds).  No position is ever taken
+//          from an atomic, so the result depends on the routing alone (an
+//          activation-checkpoint replay of the same routing reproduces it
+//          bit for bit).  Global stores come after the last workgroup
+//          barrier: a barrier waits for the workgroup's outstanding stores.
 //
 // Ids outside [0,E) go to an extra bucket E, sorted after every expert, so
 // that every position stays inside [0, T*K) even for bad input; the rank
@@ -32,15 +36,14 @@ namespace {
 
 constexpr int kLT = kLayoutThreads;  // threads per layout workgroup
 constexpr int kLW = kLT / kWave;     // waves per layout workgroup
-constexpr int kScanRegs = 24;        // histogram entries a thread holds in registers
+constexpr int kColRegs = 64;         // histogram tiles a scan thread loads at once
+constexpr int kIdRegs = 2;           // tile ids a thread loads before the scan
+
+__device__ __forceinline__ int clamp_id(long long v, int E) { return (v >= 0 && v < E) ? (int)v : E; }
 
 __device__ __forceinline__ int load_expert(const void* idx, int itype, int64_t i, int E) {
-  if (itype == MOE_I32) {
-    const int v = static_cast<const int*>(idx)[i];
-    return (v >= 0 && v < E) ? v : E;
-  }
-  const long long v = static_cast<const long long*>(idx)[i];
-  return (v >= 0 && v < (long long)E) ? (int)v : E;
+  if (itype == MOE_I32) return clamp_id(static_cast<const int*>(idx)[i], E);
+  return clamp_id(static_cast<const long long*>(idx)[i], E);
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
@@ -58,6 +61,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
   extern __shared__ __align__(8) unsigned char smem[];
   const int E1 = a.E + 1;
+  const int NR = E1 + a.P;
   unsigned long long* msk = reinterpret_cast<unsigned long long*>(smem);  // [tile]
   int* eh = reinterpret_cast<int*>(msk + a.tile);                        // [E+1]
   int* rh = eh + E1;                                                     // [P]
@@ -65,14 +69,13 @@ __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
   const int b = blockIdx.x;
   const int t0 = b * a.tile;
   const int nt = max(0, min(a.T, t0 + a.tile) - t0);
-  for (int i = tid; i < E1 + a.P; i += kLT) eh[i] = 0;
+  for (int i = tid; i < NR; i += kLT) eh[i] = 0;
   for (int i = tid; i < nt; i += kLT) msk[i] = 0ull;
-  if (b == 0 && tid == 0) *a.status = 0;  // later kernels only OR bits in
   __syncthreads();
 
   const int np = nt * a.K;
   const int64_t p0 = (int64_t)t0 * a.K;
-#pragma unroll 8
+#pragma unroll 4
   for (int i = tid; i < np; i += kLT) {
     const int e = load_expert(a.idx, a.itype, p0 + i, a.E);
     atomicAdd(&eh[e], 1);
@@ -88,97 +91,100 @@ __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
       atomicAdd(&rh[r], 1);
     }
   }
-  // is_token_in_rank: whole 32-bit words, then the tail bytes (t0*P is a
-  // multiple of 64 because the tile is)
-  uint32_t* itr_w = reinterpret_cast<uint32_t*>(a.is_token_in_rank + (size_t)t0 * a.P);
+  __syncthreads();  // before any global store (a barrier would wait for them)
+
+  for (int tt = tid; tt < nt; tt += kLT) a.tok_mask[t0 + tt] = msk[tt];
   const int nbytes = nt * a.P;
-  for (int wd = tid; wd < nbytes / 4; wd += kLT) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = wd * 4 + q;
-      const int tt = i / a.P;
-      v |= (uint32_t)((msk[tt] >> (i - tt * a.P)) & 1ull) << (8 * q);
-    }
-    itr_w[wd] = v;
-  }
-  for (int i = (nbytes & ~3) + tid; i < nbytes; i += kLT) {
+  for (int i = tid; i < nbytes; i += kLT) {
     const int tt = i / a.P;
     a.is_token_in_rank[(size_t)t0 * a.P + i] = (uint8_t)((msk[tt] >> (i - tt * a.P)) & 1ull);
   }
-  __syncthreads();
-
-  for (int r = tid; r < E1 + a.P; r += kLT) a.hist[(size_t)r * a.nblk + b] = eh[r];
+  for (int r = tid; r < NR; r += kLT) a.hist[(size_t)b * NR + r] = eh[r];
+  if (b == 0 && tid == 0) *a.status = 0;  // later kernels only OR bits in
 }
 
 // ---- rank -------------------------------------------------------------------
 
-// Exclusive scan, by the whole workgroup, of the [rows][nblk] histogram read
-// row-major.  At (row, j) it is the row's global start plus the row's count
-// in the tiles before j.  Writes column b to col_b[rows], column 0 to
-// col_0[rows] and the total to col_0[rows].
-__device__ void scan_histogram(const int* __restrict__ h, int rows, int nblk, int b, int* col_b,
-                               int* col_0, int* wsum) {
+// Start of every histogram column, globally and at tile b.  The histogram is
+// tile-major, h[j * NR + r]: count of column r (a bucket, then a partition)
+// in tile j.  Writes col_0[r] = sum of all columns before r (col_0[NR] = the
+// total) and col_b[r] = col_0[r] + column r's count in the tiles before b.
+// Each thread sums a range of tiles of one column with all its loads in
+// flight (clamped, unconditional loads); a workgroup scan over the column
+// totals follows.  part: LDS [2][parts][NR].  Ends with a barrier.
+__device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int b, int* col_b,
+                               int* col_0, int* part, int* wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
-  const int n = rows * nblk;
-  const int per = (n + kLT - 1) / kLT;
-  const int i0 = min(n, tid * per);
-  const int i1 = min(n, i0 + per);
-  // the first kScanRegs entries of the run stay in registers (all loads in
-  // flight together); longer runs are re-read in the second walk
-  int hv[kScanRegs];
+  const int parts = max(1, min(nblk, kLT / NR));  // threads per column
+  const int cpp = (nblk + parts - 1) / parts;     // tiles per thread
+  for (int item = tid; item < NR * parts; item += kLT) {
+    const int q = item / NR;
+    const int r = item - q * NR;
+    const int j0 = q * cpp;
+    const int j1 = min(nblk, j0 + cpp);
+    int tot = 0, pre = 0;
+    for (int c0 = j0; c0 < j1; c0 += kColRegs) {
+      int v[kColRegs];
 #pragma unroll
-  for (int u = 0; u < kScanRegs; ++u) hv[u] = (i0 + u < i1) ? h[i0 + u] : 0;
-  int s = 0;
+      for (int u = 0; u < kColRegs; ++u) v[u] = h[(size_t)min(c0 + u, j1 - 1) * NR + r];
 #pragma unroll
-  for (int u = 0; u < kScanRegs; ++u) s += hv[u];
-  for (int i = i0 + kScanRegs; i < i1; ++i) s += h[i];
-
-  const int inc = wave_inclusive_scan(s);
-  if (lane == kWave - 1) wsum[wv] = inc;
-  __syncthreads();
-  int run = inc - s;
-  for (int w = 0; w < wv; ++w) run += wsum[w];
-  int row = i0 / nblk;
-  int j = i0 - row * nblk;
-#pragma unroll
-  for (int u = 0; u < kScanRegs; ++u) {
-    if (i0 + u < i1) {
-      if (j == 0) col_0[row] = run;
-      if (j == b) col_b[row] = run;
-      run += hv[u];
-      if (++j == nblk) {
-        j = 0;
-        ++row;
+      for (int u = 0; u < kColRegs; ++u) {
+        const int x = (c0 + u < j1) ? v[u] : 0;
+        tot += x;
+        pre += (c0 + u < b) ? x : 0;
       }
     }
+    part[q * NR + r] = tot;
+    part[(parts + q) * NR + r] = pre;
   }
-  for (int i = i0 + kScanRegs; i < i1; ++i) {
-    if (j == 0) col_0[row] = run;
-    if (j == b) col_b[row] = run;
-    run += h[i];
-    if (++j == nblk) {
-      j = 0;
-      ++row;
+  __syncthreads();
+  int carry = 0;
+  for (int c0 = 0; c0 < NR; c0 += kLT) {  // uniform
+    const int r = c0 + tid;
+    int tot = 0, pre = 0;
+    if (r < NR) {
+      for (int q = 0; q < parts; ++q) {
+        tot += part[q * NR + r];
+        pre += part[(parts + q) * NR + r];
+      }
     }
+    const int inc = wave_inclusive_scan(tot);
+    if (lane == kWave - 1) wsum[wv] = inc;
+    __syncthreads();
+    int st = carry + inc - tot, all = 0;
+#pragma unroll
+    for (int w = 0; w < kLW; ++w) {
+      const int ws = wsum[w];
+      if (w < wv) st += ws;
+      all += ws;
+    }
+    if (r < NR) {
+      col_0[r] = st;
+      col_b[r] = st + pre;
+    }
+    carry += all;
+    __syncthreads();  // wsum is rewritten by the next chunk
   }
-  if (i0 < i1 && i1 == n) col_0[rows] = run;
+  if (tid == 0) col_0[NR] = carry;
   __syncthreads();
 }
 
 __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   extern __shared__ __align__(8) unsigned char smem[];
   const int E1 = a.E + 1;
-  const int NR = E1 + a.P;                   // histogram rows
-  int* base = reinterpret_cast<int*>(smem);  // [NR]   this tile's start of each row
-  int* off = base + NR;                      // [NR+1] start of each row, tile 0
+  const int NR = E1 + a.P;                   // histogram columns
+  const int parts = max(1, min(a.nblk, kLT / NR));
+  int* base = reinterpret_cast<int*>(smem);  // [NR]   this tile's start of each column
+  int* off = base + NR;                      // [NR+1] start of each column, tile 0
   int* cnt = off + NR + 1;                   // [kLW][E+1] per-wave bucket cursors
   int* wsum = cnt + kLW * E1;                // [kLW]
   int* wcnt = wsum + kLW;                    // [kLW][P] per-wave partition counts
-  int* carry = wcnt + kLW * a.P;             // [P] slots used by earlier token rounds
-  uint16_t* ids = reinterpret_cast<uint16_t*>(carry + a.P);  // [tile*K]
+  int* wpre = wcnt + kLW * a.P;              // [kLW][P] slots before each wave
+  int* carry = wpre + kLW * a.P;             // [P] slots used by earlier token rounds
+  int* part = carry + a.P;                   // [2][parts][NR] scan partials
+  uint16_t* ids = reinterpret_cast<uint16_t*>(part + 2 * parts * NR);  // [tile*K]
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -189,26 +195,37 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   const int np = nt * a.K;
   const int64_t p0 = (int64_t)t0 * a.K;
 
-  // 0. stage this tile's ids (bad ids become bucket E)
-#pragma unroll 8
-  for (int i = tid; i < np; i += kLT) ids[i] = (uint16_t)load_expert(a.idx, a.itype, p0 + i, a.E);
+  // 0. loads whose round trips overlap the scan's: the first kIdRegs ids of
+  //    each thread and the first round's token masks (clamped, unconditional
+  //    loads; the range checks are applied later)
+  long long idv[kIdRegs];
+  unsigned long long m0 = 0ull;
+  if (np > 0) {  // uniform
+    if (a.itype == MOE_I32) {
+      const int* src = static_cast<const int*>(a.idx) + p0;
+#pragma unroll
+      for (int u = 0; u < kIdRegs; ++u) idv[u] = src[min(tid + u * kLT, np - 1)];
+    } else {
+      const long long* src = static_cast<const long long*>(a.idx) + p0;
+#pragma unroll
+      for (int u = 0; u < kIdRegs; ++u) idv[u] = src[min(tid + u * kLT, np - 1)];
+    }
+    m0 = a.tok_mask[t0 + min(tid, nt - 1)];
+  }
   for (int r = tid; r < a.P; r += kLT) carry[r] = 0;
 
   // 1. global offsets and this tile's starts (the scan ends with a barrier)
-  scan_histogram(a.hist, NR, a.nblk, b, base, off, wsum);
-  const int total = off[E1];  // T*K: the bucket rows come first
-
-  // 2. global counts and offsets (tile 0 writes them)
-  if (b == 0) {
-    for (int e = tid; e < a.E; e += kLT) a.num_tokens_per_expert[e] = off[e + 1] - off[e];
-    for (int e = tid; e <= a.E; e += kLT) a.expert_offset[e] = off[e];
-    for (int r = tid; r <= a.P; r += kLT) a.rank_offset[r] = off[r * a.epr];
-    for (int r = tid; r < a.P; r += kLT) a.num_tokens_per_rank[r] = off[E1 + r + 1] - off[E1 + r];
-    for (int r = tid; r <= a.P; r += kLT) a.send_offset[r] = off[E1 + r] - total;
-    if (tid == 0 && off[a.E + 1] != off[a.E]) atomicOr(a.status, MOE_STATUS_BAD_EXPERT);
+  scan_histogram(a.hist, NR, a.nblk, b, base, off, part, wsum);
+#pragma unroll
+  for (int u = 0; u < kIdRegs; ++u) {
+    const int i = tid + u * kLT;
+    if (i < np) ids[i] = (uint16_t)clamp_id(idv[u], a.E);
   }
+  for (int i = tid + kIdRegs * kLT; i < np; i += kLT)
+    ids[i] = (uint16_t)load_expert(a.idx, a.itype, p0 + i, a.E);
+  __syncthreads();
 
-  // 3. per-wave bucket counts over contiguous pair spans of the tile
+  // 2. per-wave bucket counts over contiguous pair spans of the tile
   const int span = (((np + kLW - 1) / kLW) + kWave - 1) & ~(kWave - 1);
   const int w_lo = min(np, wv * span);
   const int w_hi = min(np, w_lo + span);
@@ -218,16 +235,56 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   for (int i = w_lo + lane; i < w_hi; i += kWave) atomicAdd(&mycnt[ids[i]], 1);
   __syncthreads();
 
-  // 4. first receive row of each (wave, bucket)
+  // 3. first receive row of each (wave, bucket)
   for (int e = tid; e < E1; e += kLT) {
+    int c[kLW];
+#pragma unroll
+    for (int w = 0; w < kLW; ++w) c[w] = cnt[w * E1 + e];
     int run = base[e];
+#pragma unroll
     for (int w = 0; w < kLW; ++w) {
-      const int c = cnt[w * E1 + e];
       cnt[w * E1 + e] = run;
-      run += c;
+      run += c[w];
     }
   }
   __syncthreads();
+
+  // 4. token send slots, one token per thread per round: per partition, a
+  //    ballot ranks the round's tokens inside each wave, and a table of
+  //    per-wave starts places the waves
+  for (int c0 = 0; c0 < nt; c0 += kLT) {  // uniform
+    const int tt = c0 + tid;
+    const unsigned long long m = tt < nt ? (c0 == 0 ? m0 : a.tok_mask[t0 + tt]) : 0ull;
+    for (int r = 0; r < a.P; ++r) {
+      const uint64_t bal = __ballot((int)((m >> r) & 1ull));
+      if (lane == 0) wcnt[wv * a.P + r] = __popcll(bal);
+    }
+    __syncthreads();
+    for (int item = tid; item < kLW * a.P; item += kLT) {
+      const int w = item / a.P;
+      const int r = item - w * a.P;
+      int s = carry[r] + base[E1 + r] - off[E1 + r];
+#pragma unroll
+      for (int u = 0; u < kLW; ++u) {
+        const int c = wcnt[u * a.P + r];
+        if (u < w) s += c;
+      }
+      wpre[item] = s;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < a.P; ++r) {  // uniform: every lane takes part in the ballot
+      const int on = (int)((m >> r) & 1ull);
+      const uint64_t bal = __ballot(on);
+      const int slot = wpre[wv * a.P + r] + __popcll(bal & lanes_below(lane));
+      if (tt < nt) a.token_slot[(size_t)(t0 + tt) * a.P + r] = on ? slot : -1;
+    }
+    if (c0 + kLT < nt) {  // more rounds (very large tiles only): carry the counts
+      for (int r = tid; r < a.P; r += kLT)
+        carry[r] = wpre[(kLW - 1) * a.P + r] + wcnt[(kLW - 1) * a.P + r] - (base[E1 + r] - off[E1 + r]);
+      __syncthreads();
+    }
+  }
 
   // 5. stable rank, 64 pairs at a time (all lanes of the wave take part)
   const int R = a.T * a.K;
@@ -249,56 +306,29 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
       const int pos = start + rank;
       const int64_t pair = p0 + i;
       if ((unsigned)pos < (unsigned)R) {
-        const int t = (int)(pair / a.K);
+        const int tq = i / a.K;
         a.recv_pos[pair] = pos;
-        a.recv_token[pos] = t;
-        a.recv_k[pos] = (int)(pair - (int64_t)t * a.K);
+        a.recv_token[pos] = t0 + tq;
+        a.recv_k[pos] = i - tq * a.K;
       } else {
         atomicOr(a.status, MOE_STATUS_BAD_POSITION);
       }
     }
-    // the highest lane of each group moves the counter past the group; the
+    // the highest lane of each group moves the cursor past the group; the
     // wave barrier keeps the next round's reads after this write
     if (act && (same >> lane) == 1ull) mycnt[e] = start + __popcll(same);
     __builtin_amdgcn_wave_barrier();
   }
 
-  // 6. token send slots, one token per thread per round: per partition, a
-  //    ballot ranks the round's tokens inside each wave, and the per-wave
-  //    counts give each wave its start
-  for (int c0 = 0; c0 < nt; c0 += kLT) {  // uniform
-    const int tt = c0 + tid;
-    unsigned long long m = 0;
-    if (tt < nt) {
-      for (int k = 0; k < a.K; ++k) {
-        const int e = ids[tt * a.K + k];
-        if (e < a.E) m |= 1ull << (e / a.epr);
-      }
-    }
-    for (int r = 0; r < a.P; ++r) {
-      const uint64_t bal = __ballot((int)((m >> r) & 1ull));
-      if (lane == 0) wcnt[wv * a.P + r] = __popcll(bal);
-    }
-    __syncthreads();
-    for (int r = 0; r < a.P; ++r) {  // uniform: every lane takes part in the ballot
-      const int on = (int)((m >> r) & 1ull);
-      const uint64_t bal = __ballot(on);
-      if (tt < nt) {
-        int slot = -1;
-        if (on) {
-          slot = base[E1 + r] - off[E1 + r] + carry[r] + __popcll(bal & lanes_below(lane));
-          for (int w = 0; w < wv; ++w) slot += wcnt[w * a.P + r];
-        }
-        a.token_slot[(size_t)(t0 + tt) * a.P + r] = slot;
-      }
-    }
-    __syncthreads();
-    for (int r = tid; r < a.P; r += kLT) {
-      int s = 0;
-      for (int w = 0; w < kLW; ++w) s += wcnt[w * a.P + r];
-      carry[r] += s;
-    }
-    __syncthreads();
+  // 6. global counts, offsets and status (tile 0 writes them)
+  if (b == 0) {
+    const int total = off[E1];  // T*K: the bucket columns come first
+    for (int e = tid; e < a.E; e += kLT) a.num_tokens_per_expert[e] = off[e + 1] - off[e];
+    for (int e = tid; e <= a.E; e += kLT) a.expert_offset[e] = off[e];
+    for (int r = tid; r <= a.P; r += kLT) a.rank_offset[r] = off[r * a.epr];
+    for (int r = tid; r < a.P; r += kLT) a.num_tokens_per_rank[r] = off[E1 + r + 1] - off[E1 + r];
+    for (int r = tid; r <= a.P; r += kLT) a.send_offset[r] = off[E1 + r] - total;
+    if (tid == 0 && off[a.E + 1] != off[a.E]) atomicOr(a.status, MOE_STATUS_BAD_EXPERT);
   }
 }
 
@@ -310,7 +340,8 @@ size_t layout_count_lds(int E, int P, int tile) {
 
 size_t layout_rank_lds(int E, int P, int tile, int K) {
   const size_t E1 = (size_t)E + 1, NR = E1 + P;
-  const size_t ints = NR + (NR + 1) + kLW * E1 + kLW + (size_t)kLW * P + P;
+  const size_t parts_nr = NR > (size_t)kLT ? NR : (size_t)kLT;  // parts * NR <= max(kLT, NR)
+  const size_t ints = NR + (NR + 1) + kLW * E1 + kLW + 2 * (size_t)kLW * P + P + 2 * parts_nr;
   return ints * 4 + (size_t)tile * K * 2;
 }
 
