@@ -86,16 +86,20 @@ def kernel_source_hash():
 
 
 def traffic_from_profiles(kernel: str):
-    """HBM traffic per launch from the committed counter runs, if they are current."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known size), or None
+    when the kernels have changed since the counters were taken."""
+    import re
+
+    path = os.path.join(ROOT, "profiles", "traffic_qwen3_30b_a3b.md")
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        d = json.load(f)
-    if d.get("source_hash") != kernel_source_hash():
-        return None  # kernels changed since the counters were taken
-    k = d.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    text = open(path).read()
+    m = re.search(r"^source_hash: (\w+)$", text, re.M)
+    if m is None or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(r"^traffic_bytes_per_launch\.%s: (\d+)$" % re.escape(kernel), text, re.M)
+    return None if m is None else int(m.group(1))
 
 
 class HipEvents:
