@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--chunks-per-lane", type=int, default=0)
     ap.add_argument("--nontemporal", type=int, default=1)
     ap.add_argument("--waves-per-block", type=int, default=0)
+    ap.add_argument("--layout-pairs", type=int, default=0)
     ap.add_argument("--events", choices=["all", "dominant", "none"], default="dominant",
                     help="HIP events in the timed region: around every call, around the "
                          "dominant kernel's call only, or none")
@@ -228,7 +229,7 @@ def main():
         s["grad_w"] = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device=dev)
         s["grad_x"] = torch.empty((cfg.T, cfg.H), dtype=tdt, device=dev)
         s["ws"] = torch.empty(M.moe_workspace_size(cfg.T, cfg.K, cfg.E, cfg.P), dtype=torch.uint8, device=dev)
-        s["h"] = M.Handle(args.chunks_per_lane, args.nontemporal, args.waves_per_block)
+        s["h"] = M.Handle(args.chunks_per_lane, args.nontemporal, args.waves_per_block, args.layout_pairs)
         sets.append(s)
     del x0, y0, g0, gr0
     torch.cuda.synchronize()
@@ -349,7 +350,7 @@ def main():
             "timing": ("hip graph replay" if graphs is not None else "eager launches") +
                       f", events: {args.events if graphs is None else 'none'}",
             "tuning": {"chunks_per_lane": args.chunks_per_lane, "nontemporal": args.nontemporal,
-                       "waves_per_block": args.waves_per_block},
+                       "waves_per_block": args.waves_per_block, "layout_pairs": args.layout_pairs},
         },
         "roofline": None if achieved is None else {
             "bound": "hbm",

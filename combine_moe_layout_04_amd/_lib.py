@@ -16,7 +16,8 @@ c_char_p = ctypes.c_char_p
 
 
 class MoeTuning(ctypes.Structure):
-    _fields_ = [("chunks_per_lane", c_int), ("nontemporal", c_int), ("waves_per_block", c_int)]
+    _fields_ = [("chunks_per_lane", c_int), ("nontemporal", c_int), ("waves_per_block", c_int),
+                ("layout_pairs", c_int)]
 
 
 # name -> (restype, argtypes); the functions declared in include/moe_layout.h

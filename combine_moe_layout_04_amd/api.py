@@ -81,8 +81,9 @@ def moe_workspace_size(T: int, K: int, E: int, P: int) -> int:
 class Handle:
     """Opaque layout handle plus the device workspace its arrays live in."""
 
-    def __init__(self, chunks_per_lane: int = 0, nontemporal: int = 1, waves_per_block: int = 0):
-        tun = MoeTuning(chunks_per_lane, nontemporal, waves_per_block)
+    def __init__(self, chunks_per_lane: int = 0, nontemporal: int = 1, waves_per_block: int = 0,
+                 layout_pairs: int = 0):
+        tun = MoeTuning(chunks_per_lane, nontemporal, waves_per_block, layout_pairs)
         h = ctypes.c_void_p()
         _check(lib().moe_handle_create(ctypes.byref(h), ctypes.byref(tun)), "moe_handle_create")
         self._h = h

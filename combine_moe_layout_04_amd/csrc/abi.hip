@@ -21,10 +21,11 @@ namespace moe {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-WsLayout plan_workspace(int64_t T, int K, int E, int P) {
+WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs) {
   WsLayout w{};
-  // Token tiles of the layout: at most 512 (t,k) pairs per tile (one per
-  // thread of a layout workgroup), unless that needs more than 128 tiles;
+  // Token tiles of the layout: at most layout_pairs (t,k) pairs per tile
+  // (512: one per thread of a layout workgroup), unless that needs more
+  // than 128 tiles;
   // then ~128 tiles, each wave of a tile looping over rounds of 64 pairs.
   // Capped by the LDS the rank kernel stages the tile's ids in (2 bytes per
   // pair, within 64 KiB with its other arrays) and the count kernel's per-
@@ -35,7 +36,7 @@ WsLayout plan_workspace(int64_t T, int K, int E, int P) {
   int64_t tile_max = pair_cap / K;
   if (tile_max > 4096) tile_max = 4096;
   if (tile_max < 1) tile_max = 1;
-  int64_t tile = kLayoutThreads / K;
+  int64_t tile = layout_pairs / K;
   if (tile < 1) tile = 1;
   if ((T + tile - 1) / tile > 128) tile = (T + 127) / 128;
   if (tile > tile_max) tile = tile_max;
@@ -128,15 +129,20 @@ int moe_workspace_size(int64_t T, int K, int E, int P, size_t* bytes) {
 
 int moe_handle_create(moe_handle_t* out, const moe_tuning* tuning) {
   if (!out) return MOE_ERR_INVALID_ARG;
-  moe::Tuning t{1, 1, 4};  // defaults: one segment per wave, non-temporal receive rows, 4 waves/WG
+  // defaults: one segment per wave, non-temporal receive rows, 4 waves per
+  // workgroup, 512-pair layout tiles
+  moe::Tuning t{1, 1, 4, moe::kLayoutThreads};
   if (tuning) {
     const int c = tuning->chunks_per_lane, n = tuning->nontemporal, w = tuning->waves_per_block;
+    const int lp = tuning->layout_pairs;
     if (!(c == 0 || c == 1 || c == 2 || c == 4)) return MOE_ERR_INVALID_ARG;
     if (n < 0 || n > 2) return MOE_ERR_INVALID_ARG;
     if (!(w == 0 || w == 1 || w == 2 || w == 4 || w == 8)) return MOE_ERR_INVALID_ARG;
+    if (!(lp == 0 || lp == 512 || lp == 1024 || lp == 2048 || lp == 4096)) return MOE_ERR_INVALID_ARG;
     if (c) t.chunks_per_lane = c;
     t.nontemporal = n;
     if (w) t.waves_per_block = w;
+    if (lp) t.layout_pairs = lp;
   }
   moe_handle_s* h = new (std::nothrow) moe_handle_s();
   if (!h) return MOE_ERR_INVALID_ARG;
@@ -161,8 +167,10 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
   if (!workspace || (T > 0 && !topk_idx)) return MOE_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return MOE_ERR_ALIGNMENT;
   if (T > 0 && !aligned(topk_idx, itype == MOE_I32 ? 4 : 8)) return MOE_ERR_ALIGNMENT;
-  const moe::WsLayout plan = moe::plan_workspace(T, K, E, P);
-  if (workspace_bytes < plan.total) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < moe::plan_workspace(T, K, E, P).total) return MOE_ERR_WORKSPACE;
+  // the handle's tile size: never more tiles than the default plan sizes for
+  moe::WsLayout plan = moe::plan_workspace(T, K, E, P, h->tune.layout_pairs);
+  plan.hist = moe::plan_workspace(T, K, E, P).hist;
 
   h->has_layout = false;
   h->T = T;

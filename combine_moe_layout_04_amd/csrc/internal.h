@@ -7,6 +7,8 @@
 
 namespace moe {
 
+constexpr int kLayoutThreads = 512;  // threads per layout workgroup
+
 // Workspace sections (byte offsets from the workspace base, 256-aligned).
 struct WsLayout {
   size_t status, num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
@@ -17,9 +19,10 @@ struct WsLayout {
   int tile;  // tokens per tile
 };
 
-WsLayout plan_workspace(int64_t T, int K, int E, int P);
+// layout_pairs: (t,k) pairs per layout tile (512 sizes the workspace: more
+// pairs per tile means fewer tiles and a smaller histogram).
+WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs = kLayoutThreads);
 
-constexpr int kLayoutThreads = 512;  // threads per layout workgroup
 
 struct LayoutArgs {
   const void* idx;
@@ -90,6 +93,7 @@ struct Tuning {
   int chunks_per_lane;  // 1, 2, 4: consecutive 64-chunk segments per wave
   int nontemporal;      // 0, 1, 2
   int waves_per_block;  // 1, 2, 4, 8
+  int layout_pairs;     // 512, 1024, 2048, 4096
 };
 
 constexpr int kMaxDotWaves = 16;         // waves of one token-dot workgroup

@@ -98,6 +98,7 @@ typedef struct moe_tuning {
   int nontemporal;      /* 0: default loads/stores; 1 (default): receive-row loads and
                            stores marked non-temporal; 2: token-row stores too          */
   int waves_per_block;  /* wavefronts per workgroup of the row kernels: 0 (= 4), 1, 2, 4, 8 */
+  int layout_pairs;     /* (t,k) pairs per layout tile: 0 (= 512), 512, 1024, 2048, 4096      */
 } moe_tuning;
 
 typedef struct moe_handle_s* moe_handle_t;

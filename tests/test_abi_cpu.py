@@ -86,9 +86,10 @@ def test_handle_lifecycle_and_tuning(L):
     assert L.moe_handle_destroy(h) == C["MOE_OK"]
     assert L.moe_handle_destroy(None) == C["MOE_ERR_INVALID_ARG"]
     assert L.moe_handle_create(None, None) == C["MOE_ERR_INVALID_ARG"]
-    for bad in (MoeTuning(3, 0, 0), MoeTuning(0, 3, 0), MoeTuning(0, 0, 3)):
+    for bad in (MoeTuning(3, 0, 0, 0), MoeTuning(0, 3, 0, 0), MoeTuning(0, 0, 3, 0),
+                MoeTuning(0, 0, 0, 300), MoeTuning(0, 0, 0, 8192)):
         assert L.moe_handle_create(ctypes.byref(h), ctypes.byref(bad)) == C["MOE_ERR_INVALID_ARG"]
-    good = MoeTuning(2, 2, 8)
+    good = MoeTuning(2, 2, 8, 2048)
     assert L.moe_handle_create(ctypes.byref(h), ctypes.byref(good)) == C["MOE_OK"]
     assert L.moe_handle_destroy(h) == C["MOE_OK"]
 

@@ -104,11 +104,13 @@ def compare_layer(cfg, res, ref):
 # ------------------------------------------------------------------ layout --
 
 @pytest.mark.parametrize("name", list(W.CONFIGS))
-def test_layout_full_size(name):
+@pytest.mark.parametrize("layout_pairs", [0, 1024, 2048])
+def test_layout_full_size(name, layout_pairs):
     cfg = W.get_config(name)
-    say(f"layout {name} T={cfg.T} K={cfg.K} E={cfg.E} P={cfg.P}")
+    say(f"layout {name} T={cfg.T} K={cfg.K} E={cfg.E} P={cfg.P} layout_pairs={layout_pairs}")
     inp = W.layer_inputs(cfg, seed=0, with_rows=False)
-    h = M.moe_layout(torch.from_numpy(inp.topk_idx).to(DEV), cfg.E, cfg.P)
+    h = M.moe_layout(torch.from_numpy(inp.topk_idx).to(DEV), cfg.E, cfg.P,
+                     handle=M.Handle(layout_pairs=layout_pairs))
     assert h.check() == 0
     check_layout(h, O.layout(inp.topk_idx, cfg.E, cfg.P))
 
@@ -130,14 +132,15 @@ SMALL = [  # (T, K, E, P, distinct)
 
 
 @pytest.mark.parametrize("T,K,E,P,distinct", SMALL)
-def test_layout_shapes(T, K, E, P, distinct):
-    say(f"layout T={T} K={K} E={E} P={P} distinct={distinct}")
+@pytest.mark.parametrize("layout_pairs", [0, 4096])
+def test_layout_shapes(T, K, E, P, distinct, layout_pairs):
+    say(f"layout T={T} K={K} E={E} P={P} distinct={distinct} layout_pairs={layout_pairs}")
     rng = np.random.default_rng(T * 7 + K)
     if distinct:
         idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
     else:
         idx = rng.integers(0, E, size=(T, K)).astype(np.int32)
-    h = M.moe_layout(torch.from_numpy(idx).to(DEV), E, P)
+    h = M.moe_layout(torch.from_numpy(idx).to(DEV), E, P, handle=M.Handle(layout_pairs=layout_pairs))
     assert h.check() == 0
     check_layout(h, O.layout(idx, E, P))
 
@@ -215,8 +218,10 @@ RAGGED = [  # name, overrides
 
 @pytest.mark.parametrize("name,over", RAGGED)
 @pytest.mark.parametrize("tuning", [dict(), dict(chunks_per_lane=1, nontemporal=0, waves_per_block=1),
-                                    dict(chunks_per_lane=2, nontemporal=2, waves_per_block=8),
-                                    dict(chunks_per_lane=4, nontemporal=1, waves_per_block=2)])
+                                    dict(chunks_per_lane=2, nontemporal=2, waves_per_block=8,
+                                         layout_pairs=2048),
+                                    dict(chunks_per_lane=4, nontemporal=1, waves_per_block=2,
+                                         layout_pairs=4096)])
 def test_layer_ragged_rows_all_tunings(name, over, tuning):
     cfg = W.get_config(name, **over)
     say(f"ragged {name} {over} {tuning}")
