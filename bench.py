@@ -1,11 +1,18 @@
 """Benchmark: MoE dispatch + combine, forward + backward, per layer, on one GPU.
 
-One step is one pass of the whole hot path over one layer's synthetic input:
-layout (counts, offsets, stable positions) -> dispatch (with per-row scores)
--> combine (top-k weighted) -> combine backward (rows + router-weight
-gradient) -> dispatch backward.  The expert in between is the identity, so
-there is no GEMM: the path is HBM-bound and is measured against the HBM
-roofline.
+One step is one pass of the whole hot path over one layer's synthetic input.
+The expert in between is the identity, so there is no GEMM: the path is
+HBM-bound and is measured against the HBM roofline.
+
+* Standard layers (the default Qwen3-30B-A3B-shaped one, the skewed and the
+  DeepSeek-V3-shaped ones): layout (counts, offsets, stable positions) ->
+  dispatch (with per-row scores) -> combine (top-k weighted) -> combine
+  backward (rows + router-weight gradient) -> dispatch backward.
+* The DiffusionGemma-shaped layer (router scores absorbed before W2): three
+  forward passes with independent routings (layout, scaled dispatch, plain
+  combine); passes 1 and 3 then replay layout + dispatch (activation
+  checkpointing; the combine is never replayed) and run the combine backward
+  (a copy) and the scaled dispatch backward (rows + score gradient).
 
 Cold HBM: every kernel of a step reads buffers that were last touched more
 than 1 GB of traffic earlier (several rotating buffer sets, and the combine
@@ -23,6 +30,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "dispatch+combine fwd+bwd GB/s per layer and % of MI355X HBM peak"
 
 
 def parse():
@@ -54,28 +63,53 @@ def parse():
     return ap.parse_args()
 
 
-def layer_bytes(cfg):
-    """Algorithmic payload bytes per kernel (rows only; index traffic apart)."""
+# --------------------------------------------------------------------------
+# The step: a list of calls, each with its algorithmic row bytes
+# --------------------------------------------------------------------------
+
+def step_calls(cfg):
+    """[(name, kind, pass, algorithmic row bytes)] of one step, in order.
+
+    Row bytes only (index and weight traffic, about 4-12 bytes per (t,k)
+    pair per call, are reported apart): TH = T*H*b token-row bytes, RH =
+    T*K*H*b receive-row bytes.
+    """
     TH = cfg.T * cfg.H * cfg.esize
     RH = cfg.R * cfg.H * cfg.esize
-    R, T, K = cfg.R, cfg.T, cfg.K
-    rows = {
-        "dispatch": TH + RH,
-        "combine": RH + TH,
-        "combine_bwd": TH + 2 * RH,
-        "dispatch_bwd": RH + TH,
-        "layout": 0,
-    }
-    # index / weight traffic: recv_pos reads, weights, scores, grad_w; layout
-    # reads topk_idx and writes the handle arrays
-    index = {
-        "dispatch": R * 4 * 3,            # recv_pos, weights, recv_scores
-        "combine": R * 4 * 2,             # recv_pos, weights
-        "combine_bwd": R * 4 * 3,         # recv_pos, weights, grad_w
-        "dispatch_bwd": R * 4,            # recv_pos
-        "layout": R * 4 * 2 + R * 4 * 3 + T * cfg.P * 5 + T * 8 * 2,
-    }
-    return rows, index
+    if not cfg.absorbed:
+        return [("layout", "layout", 0, 0),
+                ("dispatch", "dispatch", 0, TH + RH),
+                ("combine", "combine", 0, RH + TH),
+                ("combine_bwd", "combine_bwd", 0, TH + 2 * RH),
+                ("dispatch_bwd", "dispatch_bwd", 0, RH + TH)]
+    calls = []
+    for p in range(3):
+        calls += [(f"layout.{p}", "layout", p, 0),
+                  (f"dispatch.{p}", "dispatch_scaled", p, TH + RH),
+                  (f"combine.{p}", "combine_plain", p, RH + TH)]
+    for p in (0, 2):
+        calls += [(f"replay_layout.{p}", "layout", p, 0),
+                  (f"replay_dispatch.{p}", "dispatch_scaled", p, TH + RH),
+                  (f"combine_bwd.{p}", "combine_bwd_plain", p, TH + RH),
+                  (f"dispatch_bwd.{p}", "dispatch_bwd_scaled", p, RH + 2 * TH)]
+    return calls
+
+
+def index_bytes(cfg):
+    """Index, weight and score traffic per step (reported apart from `value`)."""
+    R, T = cfg.R, cfg.T
+    per = {"layout": R * 4 * 2 + R * 4 * 3 + T * cfg.P * 5 + T * 8 * 2 + T * 8,
+           "dispatch": R * 4 * 3, "dispatch_scaled": R * 4 * 3, "combine": R * 4 * 2,
+           "combine_plain": R * 4, "combine_bwd": R * 4 * 3, "combine_bwd_plain": R * 4,
+           "dispatch_bwd": R * 4, "dispatch_bwd_scaled": R * 4 * 3}
+    return sum(per[kind] for _, kind, _, _ in step_calls(cfg))
+
+
+DOMINANT = "combine"  # the call whose kernel the roofline reports: the K-row gather-reduce
+
+
+def dominant_call(cfg):
+    return "combine" if not cfg.absorbed else "combine.0"
 
 
 def kernel_source_hash():
@@ -86,13 +120,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str):
+def traffic_from_profiles(cfg, kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known size), or None
     when the kernels have changed since the counters were taken."""
-    import re
-
-    path = os.path.join(ROOT, "profiles", "traffic_qwen3_30b_a3b.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -113,7 +145,6 @@ class HipEvents:
     DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, n):
-        import ctypes
         import torch
 
         torch.cuda.init()
@@ -130,14 +161,13 @@ class HipEvents:
                 raise RuntimeError("hipEventCreateWithFlags failed")
             self.ev.append(e)
         self._ms = ctypes.c_float()
-        self._byref = ctypes.byref
 
     def record(self, i, stream):
         if self.L.hipEventRecord(self.ev[i], stream) != 0:
             raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, i, j):
-        if self.L.hipEventElapsedTime(self._byref(self._ms), self.ev[i], self.ev[j]) != 0:
+        if self.L.hipEventElapsedTime(ctypes.byref(self._ms), self.ev[i], self.ev[j]) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return self._ms.value
 
@@ -147,39 +177,67 @@ class HipEvents:
         self.ev = []
 
 
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle, untuned, on a bounded sample of the same step
+# --------------------------------------------------------------------------
+
 def cpu_baseline(cfg, budget_s):
-    """The oracle, untuned, on a bounded sample: whole layers of the same shape."""
-    import numpy as np
+    import numpy as np  # noqa: F401
 
     import workloads as W
     from oracle import moe_oracle as O
 
-    inp = W.layer_inputs(cfg, seed=0)
     dt = cfg.dtype
-    w = inp.topk_weights
-    rows, _ = layer_bytes(cfg)
-    per_layer = sum(rows.values())
-    n = 0
+    passes = 3 if cfg.absorbed else 1
+    inps = [W.layer_inputs(cfg, seed=0, pss=p) for p in range(passes)]
+    calls = step_calls(cfg)
+    step_b = sum(b for _, _, _, b in calls)
+    lay = {}
+    n_calls, moved = 0, 0
     t0 = time.perf_counter()
-    while True:
-        lay = O.layout(inp.topk_idx, cfg.E, cfg.P)
-        O.dispatch(lay, inp.x, dt, w)
-        O.combine(lay, inp.y, dt, w)
-        O.combine_bwd(lay, inp.g, dt, w, inp.y)
-        O.dispatch_bwd(lay, inp.grad_recv, dt)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
-            break
+    out_of_time = False
+    # the step's calls in order, step after step, until the budget is spent
+    while not out_of_time and n_calls < 50 * len(calls):
+        for name, kind, p, b in calls:
+            inp = inps[p]
+            w = inp.topk_weights
+            if kind == "layout":
+                lay[p] = O.layout(inp.topk_idx, cfg.E, cfg.P)
+            elif kind == "dispatch":
+                O.dispatch(lay[p], inp.x, dt, w)
+            elif kind == "dispatch_scaled":
+                O.dispatch(lay[p], inp.x, dt, w, scale_rows=True)
+            elif kind == "combine":
+                O.combine(lay[p], inp.y, dt, w)
+            elif kind == "combine_plain":
+                O.combine(lay[p], inp.y, dt)
+            elif kind == "combine_bwd":
+                O.combine_bwd(lay[p], inp.g, dt, w, inp.y)
+            elif kind == "combine_bwd_plain":
+                O.combine_bwd(lay[p], inp.g, dt)
+            elif kind == "dispatch_bwd":
+                O.dispatch_bwd(lay[p], inp.grad_recv, dt)
+            elif kind == "dispatch_bwd_scaled":
+                O.dispatch_bwd(lay[p], inp.grad_recv, dt, w, inp.x)
+            n_calls += 1
+            moved += b
+            if time.perf_counter() - t0 >= budget_s:
+                out_of_time = True
+                break
+    done_steps = n_calls // len(calls)
+    el = time.perf_counter() - t0
     return {
-        "value": round(per_layer * n / el / 1e9, 3),
+        "value": round(moved / el / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{n} full {cfg.name} layers (T={cfg.T}, H={cfg.H}, {dt}) fwd+bwd, "
-                  f"numpy single-threaded, {el:.1f} s, {el / n * 1e3:.0f} ms/layer",
+        "sample": f"{done_steps} whole steps + {n_calls - done_steps * len(calls)} calls of the "
+                  f"{cfg.name} step (T={cfg.T}, H={cfg.H}, {dt}; {step_b / 1e6:.1f} MB of rows per step), "
+                  f"numpy single-threaded, {el:.1f} s",
     }
 
+
+# --------------------------------------------------------------------------
 
 def main():
     args = parse()
@@ -203,63 +261,96 @@ def main():
     cfg = W.get_config(args.config)
     dt = cfg.dtype
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    passes = 3 if cfg.absorbed else 1
 
     def dev_rows(a):
         if dt == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    inp = W.layer_inputs(cfg, seed=0)
-    idx0 = torch.from_numpy(inp.topk_idx).to(dev)
-    w0 = torch.from_numpy(inp.topk_weights).to(dev)
-    x0, y0, g0, gr0 = (dev_rows(a) for a in (inp.x, inp.y, inp.g, inp.grad_recv))
-    del inp
+    # inputs: per pass a routing and token rows; expert outputs and
+    # gradients are shared by the passes
+    base = W.layer_inputs(cfg, seed=0)
+    y0, g0, gr0 = (dev_rows(a) for a in (base.y, base.g, base.grad_recv))
+    per_pass = []
+    for p in range(passes):
+        inp = base if p == 0 else W.layer_inputs(cfg, seed=0, pss=p, with_rows=False)
+        x = dev_rows(base.x if p == 0 else W.normal_rows(cfg, cfg.T, 1, seed=0, pss=p))
+        per_pass.append((torch.from_numpy(inp.topk_idx).to(dev), torch.from_numpy(inp.topk_weights).to(dev), x))
+    del base
+
+    def empty_rows(n):
+        return torch.empty((n, cfg.H), dtype=tdt, device=dev)
 
     nsets = 1 if args.warm else max(1, args.sets)
+    ws_bytes = M.moe_workspace_size(cfg.T, cfg.K, cfg.E, cfg.P)
     sets = []
     for _ in range(nsets):
-        s = dict(idx=idx0.clone(), w=w0.clone(), x=x0.clone(), y=y0.clone(), g=g0.clone())
+        s = {"pass": [], "y": y0.clone(), "g": g0.clone()}
         if not args.warm:
             s["y_bwd"] = y0.clone()      # the backward's own copy of the expert output
             s["grad_recv"] = gr0.clone()
-        s["recv"] = torch.empty((cfg.R, cfg.H), dtype=tdt, device=dev)
-        s["scores"] = torch.empty(cfg.R, dtype=torch.float32, device=dev)
-        s["out"] = torch.empty((cfg.T, cfg.H), dtype=tdt, device=dev)
-        s["grad_y"] = torch.empty((cfg.R, cfg.H), dtype=tdt, device=dev)
+        for idx, w, x in per_pass:
+            s["pass"].append(dict(
+                idx=idx.clone(), w=w.clone(), x=x.clone(),
+                recv=empty_rows(cfg.R), scores=torch.empty(cfg.R, dtype=torch.float32, device=dev),
+                out=empty_rows(cfg.T),
+                ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
+                h=M.Handle(args.chunks_per_lane, args.nontemporal, args.waves_per_block, args.layout_pairs)))
+        s["grad_y"] = empty_rows(cfg.R)
         s["grad_w"] = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device=dev)
-        s["grad_x"] = torch.empty((cfg.T, cfg.H), dtype=tdt, device=dev)
-        s["ws"] = torch.empty(M.moe_workspace_size(cfg.T, cfg.K, cfg.E, cfg.P), dtype=torch.uint8, device=dev)
-        s["h"] = M.Handle(args.chunks_per_lane, args.nontemporal, args.waves_per_block, args.layout_pairs)
+        s["grad_x"] = empty_rows(cfg.T)
         sets.append(s)
-    del x0, y0, g0, gr0
+    del y0, g0, gr0, per_pass
     torch.cuda.synchronize()
 
-    names = ["layout", "dispatch", "combine", "combine_bwd", "dispatch_bwd"]
-    DOMINANT = "combine"  # the longest single kernel (a K-row gather-reduce)
+    calls = step_calls(cfg)
+    names = [c[0] for c in calls]
+    ncall = len(calls)
+    dom = dominant_call(cfg)
 
-    def step_call(s, ev=None, only=None):
-        def mark(i):
-            if ev is not None and (only is None or i in only):
-                hev.record(ev + i, stream)
-        mark(0)
-        h = M.moe_layout(s["idx"], cfg.E, cfg.P, handle=s["h"], workspace=s["ws"])
-        mark(1)
-        M.moe_dispatch(h, s["x"], s["w"], recv=s["recv"], recv_scores=s["scores"])
-        mark(2)
-        y = s["recv"] if args.warm else s["y"]
-        M.moe_combine(h, y, s["w"], out=s["out"])
-        mark(3)
-        yb = s["recv"] if args.warm else s["y_bwd"]
-        M.moe_combine_bwd(h, s["g"], s["w"], yb, grad_y=s["grad_y"], grad_w=s["grad_w"])
-        mark(4)
-        gr = s["grad_y"] if args.warm else s["grad_recv"]
-        M.moe_dispatch_bwd(h, gr, None, None, grad_x=s["grad_x"])
-        mark(5)
+    def run_call(s, kind, p):
+        q = s["pass"][p]
+        h = q["h"]
+        if kind == "layout":
+            M.moe_layout(q["idx"], cfg.E, cfg.P, handle=h, workspace=q["ws"])
+        elif kind == "dispatch":
+            M.moe_dispatch(h, q["x"], q["w"], recv=q["recv"], recv_scores=q["scores"])
+        elif kind == "dispatch_scaled":
+            M.moe_dispatch(h, q["x"], q["w"], scale_rows=True, recv=q["recv"], recv_scores=q["scores"])
+        elif kind in ("combine", "combine_plain"):
+            y = q["recv"] if args.warm else s["y"]
+            M.moe_combine(h, y, q["w"] if kind == "combine" else None, out=q["out"])
+        elif kind == "combine_bwd":
+            yb = q["recv"] if args.warm else s["y_bwd"]
+            M.moe_combine_bwd(h, s["g"], q["w"], yb, grad_y=s["grad_y"], grad_w=s["grad_w"])
+        elif kind == "combine_bwd_plain":
+            M.moe_combine_bwd(h, s["g"], grad_y=s["grad_y"])
+        elif kind == "dispatch_bwd":
+            gr = s["grad_y"] if args.warm else s["grad_recv"]
+            M.moe_dispatch_bwd(h, gr, grad_x=s["grad_x"])
+        elif kind == "dispatch_bwd_scaled":
+            gr = s["grad_y"] if args.warm else s["grad_recv"]
+            M.moe_dispatch_bwd(h, gr, q["w"], q["x"], grad_x=s["grad_x"], grad_s=s["grad_w"])
+        else:
+            raise ValueError(kind)
 
+    def step(s, base=None):
+        # base: first event index of this step (events bracket the timed calls)
+        for j, (_, kind, p, _) in enumerate(calls):
+            slot = None if base is None else slot_of.get(j)
+            if slot is not None:
+                hev.record(base + 2 * slot, stream)
+            run_call(s, kind, p)
+            if slot is not None:
+                hev.record(base + 2 * slot + 1, stream)
+
+    slot_of = {}
     for i in range(args.warmup):
-        step_call(sets[i % nsets])
+        step(sets[i % nsets])
     for s in sets:
-        assert s["h"].check() == 0
+        for q in s["pass"]:
+            assert q["h"].check() == 0
 
     graphs = None
     if args.graph:
@@ -268,30 +359,33 @@ def main():
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
             for s in sets:
-                step_call(s)  # warm the capture stream
+                step(s)  # warm the capture stream
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
         for s in sets:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step_call(s)
+                step(s)
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % nsets].replay()
         torch.cuda.synchronize()
 
     K = args.steps
-    d = names.index(DOMINANT)
-    only = None if args.events == "all" else ({d, d + 1} if args.events == "dominant" else set())
+    d = names.index(dom)
+    timed = [] if graphs is not None or args.events == "none" else (
+        list(range(ncall)) if args.events == "all" else [d])
+    slot_of = {j: r for r, j in enumerate(timed)}
+    per_step = 2 * len(timed)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    hev = HipEvents(6 * K)
+    hev = HipEvents(per_step * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         if graphs is not None:
             graphs[i % nsets].replay()
         else:
-            step_call(sets[i % nsets], 6 * i, only)
+            step(sets[i % nsets], per_step * i)
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -299,10 +393,8 @@ def main():
     host_us = (t_enq - t0) * 1e6 / K
 
     # per-call event times (only the calls bracketed in the timed region)
-    timed = [n for j, n in enumerate(names)
-             if graphs is None and (only is None or (j in only and j + 1 in only))]
-    call_ms = {n: [hev.elapsed_ms(6 * i + names.index(n), 6 * i + names.index(n) + 1) for i in range(K)]
-               for n in timed}
+    call_ms = {names[j]: [hev.elapsed_ms(per_step * i + 2 * r, per_step * i + 2 * r + 1) for i in range(K)]
+               for r, j in enumerate(timed)}
     hev.close()
     avg_us = {n: float(np.mean(v)) * 1e3 for n, v in call_ms.items()}
     med_us = {n: float(np.median(v)) * 1e3 for n, v in call_ms.items()}
@@ -314,16 +406,19 @@ def main():
     torch.cuda.synchronize()
     del cbuf, cdst
 
-    rows, index = layer_bytes(cfg)
-    step_bytes = sum(rows.values())
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dom = DOMINANT
+    row_bytes = {n: b for n, _, _, b in calls}
+    step_b = sum(row_bytes.values())
+    value = step_b / (ms_per_step * 1e-3) / 1e9
     dom_us = avg_us.get(dom)
-    achieved = None if dom_us is None else rows[dom] / (dom_us * 1e-6) / 1e9
-    traffic = traffic_from_profiles(dom)
+    achieved = None if dom_us is None else row_bytes[dom] / (dom_us * 1e-6) / 1e9
+    traffic = traffic_from_profiles(cfg, DOMINANT)
 
+    protocol = ("layout+dispatch+combine+combine_bwd+dispatch_bwd per step" if not cfg.absorbed else
+                "3 forward passes (layout, scaled dispatch, plain combine) + replay of layout and "
+                "dispatch and backward (combine_bwd copy, scaled dispatch_bwd with score gradient) "
+                "for passes 1 and 3, per step")
     line = {
-        "metric": "dispatch+combine fwd+bwd GB/s per layer and % of MI355X HBM peak",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -336,16 +431,15 @@ def main():
         "dtype": dt,
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: T={cfg.T} H={cfg.H} {dt} E={cfg.E} P={cfg.P} K={cfg.K}, "
-                        "layout+dispatch+combine+combine_bwd+dispatch_bwd per step",
+            "workload": f"{cfg.name}: T={cfg.T} H={cfg.H} {dt} E={cfg.E} P={cfg.P} K={cfg.K}, {protocol}",
             "cache": "warm (chained tensors)" if args.warm else f"cold ({nsets} rotating buffer sets)",
-            "bytes_per_step": step_bytes,
+            "bytes_per_step": step_b,
             "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
-            "us_per_layer": round(ms_per_step * 1e3, 2),
+            "us_per_step": round(ms_per_step * 1e3, 2),
             "call_avg_us": {n: round(v, 2) for n, v in avg_us.items()},
             "call_median_us": {n: round(v, 2) for n, v in med_us.items()},
-            "call_GBps": {n: round(rows[n] / (avg_us[n] * 1e-6) / 1e9, 1) for n in avg_us if rows[n]},
-            "index_bytes_per_step": sum(index.values()),
+            "call_GBps": {n: round(row_bytes[n] / (avg_us[n] * 1e-6) / 1e9, 1) for n in avg_us if row_bytes[n]},
+            "index_bytes_per_step": index_bytes(cfg),
             "host_enqueue_us_per_step": round(host_us, 1),
             "timing": ("hip graph replay" if graphs is not None else "eager launches") +
                       f", events: {args.events if graphs is None else 'none'}",
@@ -354,13 +448,13 @@ def main():
         },
         "roofline": None if achieved is None else {
             "bound": "hbm",
-            "kernel": dom,
+            "kernel": f"{dom} (gather_kernel: K-row gather-reduce)",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": rows[dom],
+            "algorithmic_bytes_per_launch": row_bytes[dom],
             "avg_launch_us": round(dom_us, 2),
         },
         "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds),
