@@ -126,6 +126,8 @@ __device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int 
     const int j1 = min(nblk, j0 + cpp);
     int tot = 0, pre = 0;
     for (int c0 = j0; c0 < j1; c0 += kColRegs) {
+      // clamped, unconditional loads: no branch waits on a load, so all of
+      // them are in flight together
       int v[kColRegs];
 #pragma unroll
       for (int u = 0; u < kColRegs; ++u) v[u] = h[(size_t)min(c0 + u, j1 - 1) * NR + r];
@@ -249,9 +251,22 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   }
   __syncthreads();
 
-  // 4. token send slots, one token per thread per round: per partition, a
-  //    ballot ranks the round's tokens inside each wave, and a table of
-  //    per-wave starts places the waves
+  // 4. token send slots: per partition, a ballot over the tokens ranks them.
+  //    A tile of at most 64 tokens (the usual case) is one wave's work; a
+  //    larger one takes one token per thread per round, with a table of
+  //    per-wave starts that places the waves
+  if (nt <= kWave) {  // uniform
+    if (wv == 0) {
+      const unsigned long long m = lane < nt ? m0 : 0ull;
+#pragma unroll 4
+      for (int r = 0; r < a.P; ++r) {
+        const int on = (int)((m >> r) & 1ull);
+        const uint64_t bal = __ballot(on);
+        const int slot = base[E1 + r] - off[E1 + r] + __popcll(bal & lanes_below(lane));
+        if (lane < nt) a.token_slot[(size_t)(t0 + lane) * a.P + r] = on ? slot : -1;
+      }
+    }
+  } else {
   for (int c0 = 0; c0 < nt; c0 += kLT) {  // uniform
     const int tt = c0 + tid;
     const unsigned long long m = tt < nt ? (c0 == 0 ? m0 : a.tok_mask[t0 + tt]) : 0ull;
@@ -284,6 +299,7 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
         carry[r] = wpre[(kLW - 1) * a.P + r] + wcnt[(kLW - 1) * a.P + r] - (base[E1 + r] - off[E1 + r]);
       __syncthreads();
     }
+  }
   }
 
   // 5. stable rank, 64 pairs at a time (all lanes of the wave take part)
