@@ -6,6 +6,8 @@ accumulates in float32 in the same k order.  The float32 contract (separate
 roundings, k order, canonical dot order) makes zero difference the expected
 result, so every test also asserts bitwise equality.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -281,6 +283,53 @@ def test_k_times_x_on_device():
     assert np.array_equal(as_f64(to_host(out, "bf16"), "bf16"), cfg.K * as_f64(x_np, "bf16"))
 
 
+def edge_routing(case, rng):
+    """(name, T, K, E, P, topk_idx) for layer-level edge cases."""
+    if case == "single_token_single_expert":
+        return 1, 1, 1, 1, np.zeros((1, 1), np.int32)
+    if case == "one_expert_per_partition":
+        T, K, E = 33, 3, 8
+        return T, K, E, E, np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    if case == "one_partition":
+        T, K, E = 130, 4, 16
+        return T, K, E, 1, np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    if case == "duplicate_ids":
+        T, K, E = 70, 4, 6
+        return T, K, E, 3, rng.integers(0, E, size=(T, K)).astype(np.int32)
+    if case == "all_on_one_expert":
+        T, K, E = 200, 1, 32
+        return T, K, E, 8, np.full((T, K), 31, np.int32)
+    if case == "k_equals_e":
+        T, K = 65, 8
+        return T, K, K, 4, np.tile(np.arange(K, dtype=np.int32)[::-1], (T, 1))
+    raise ValueError(case)
+
+
+EDGE = ["single_token_single_expert", "one_expert_per_partition", "one_partition", "duplicate_ids",
+        "all_on_one_expert", "k_equals_e"]
+
+
+@pytest.mark.parametrize("case", EDGE)
+@pytest.mark.parametrize("dtype,H", [("bf16", 72), ("f32", 36)])
+@pytest.mark.parametrize("absorbed", [False, True])
+def test_layer_edge_cases(case, dtype, H, absorbed):
+    rng = np.random.default_rng(zlib.crc32(f"{case}/{dtype}/{absorbed}".encode()))
+    T, K, E, P, idx = edge_routing(case, rng)
+    say(f"edge {case} T={T} K={K} E={E} P={P} {dtype} H={H} absorbed={absorbed}")
+    cfg = W.get_config("tiny").with_(T=T, H=H, dtype=dtype, E=E, P=P, K=K, absorbed=absorbed)
+    w = rng.random((T, K)).astype(np.float32)
+
+    def rows(n):
+        a = rng.standard_normal((n, H)).astype(np.float32)
+        return a if dtype == "f32" else O.f32_to_bf16(a)
+
+    inp = W.LayerInputs(cfg, idx, w, rows(T), rows(T * K), rows(T), rows(T * K))
+    h, res = run_layer(cfg, inp)
+    lay, ref = oracle_layer(cfg, inp)
+    check_layout(h, lay)
+    compare_layer(cfg, res, ref)
+
+
 # ------------------------------------------------- absorbed-score protocol --
 
 def test_diffusion_gemma_three_passes_with_replay():
@@ -372,6 +421,10 @@ def test_row_call_validation_after_layout():
     assert L.moe_combine_bwd(h.ptr, p, 1, 64, p, None, p, p, s) == -1      # ... and y
     assert L.moe_dispatch_bwd(h.ptr, p, 1, 64, p, None, p, p, s) == -1     # grad_s needs x
     assert L.moe_dispatch(h.ptr, None, 1, 64, None, 0, p, None, s) == -1
+    # router-gradient dots keep ceil(H*2/1024) * K floats in LDS (<= 64 KiB)
+    big_h = 8192 * 512 + 512  # 8193 segments of 64 chunks, K = 2: just over
+    assert L.moe_combine_bwd(h.ptr, p, 1, big_h, p, p, p, p, s) == -3
+    assert L.moe_dispatch_bwd(h.ptr, p, 1, big_h, p, p, p, p, s) == -3
     assert h.check() == 0
 
 
