@@ -62,6 +62,10 @@ __all__ = [
     "combine_bwd",
     "dispatch_bwd",
     "canonical_dot",
+    "send",
+    "expand",
+    "reduce_partitions",
+    "combine_partitions",
     "CHUNK_BYTES",
     "LANES",
 ]
@@ -146,6 +150,13 @@ class Layout:
     recv_pos: np.ndarray               # [T,K] int32, receive row of pair (t,k)
     recv_token: np.ndarray             # [R]   int32, inverse map: token of a receive row
     recv_k: np.ndarray                 # [R]   int32, inverse map: k of a receive row
+    part: np.ndarray                   # [T,K] int32, partition of pair (t,k)'s expert
+    send_token: np.ndarray             # [N_send] int32, token of each send row
+
+    @property
+    def n_send(self) -> int:
+        """Rows of the deduplicated send buffer: one per (token, partition) pair."""
+        return int(self.send_offset[-1])
 
     @property
     def R(self) -> int:
@@ -169,6 +180,8 @@ def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
       the tokens with ``is_token_in_rank[t,r]`` in increasing t; -1 if absent.
       The send row in a buffer of all partitions' lists is
       ``send_offset[r] + token_slot[t,r]``.
+    * ``send_token[s]`` is the token of send row s (the inverse of
+      ``send_offset[r] + token_slot[t,r]``).
     * ``recv_pos`` orders the pairs by expert, and within one expert by t then
       k: a stable sort of the flattened (t,k) stream by expert id.  This is
       the order the standard path's stable argsort gives, and it is a
@@ -204,6 +217,9 @@ def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
 
     running = np.cumsum(is_token_in_rank, axis=0, dtype=np.int64) - 1
     token_slot = np.where(is_token_in_rank == 1, running, -1)
+    # send rows partition by partition, tokens ascending inside each
+    send_token = np.concatenate([np.nonzero(is_token_in_rank[:, r])[0] for r in range(P)]
+                                + [np.zeros(0, np.int64)])
 
     order = np.argsort(flat, kind="stable")                  # pair ids, expert-major
     recv_pos = np.empty(R, dtype=np.int64)
@@ -224,6 +240,8 @@ def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
         recv_pos=i32(recv_pos.reshape(T, K)),
         recv_token=i32(recv_token),
         recv_k=i32(recv_k),
+        part=i32(part),
+        send_token=i32(send_token),
     )
 
 
@@ -377,3 +395,91 @@ def canonical_dot(a: np.ndarray, b: np.ndarray, dtype: str) -> np.ndarray:
     for k in range(NS):
         out = out + seg[:, k]
     return out
+
+
+# --------------------------------------------------------------------------
+# Staged exchange: a deduplicated send buffer per destination partition
+# --------------------------------------------------------------------------
+#
+# The DeepSpeed transport PR's "Why" section: the exchange sends a token once
+# per destination rank, not once per selected expert, and the receiver groups
+# what arrives by expert; its combine reduces back to token order.  Staged on
+# one GPU, the payload that would cross the link is a physical buffer
+# S[N_send, H] with one row per (token, partition) pair, at row
+# send_offset[r] + token_slot[t, r].  The combine then has two levels: each
+# partition reduces its own experts' rows of a token (what the receiver sends
+# back), and the source adds the partitions' partial rows.  Readings, since
+# the pages give the order of neither sum: the partition-level sum runs over
+# the token's k with an expert on that partition, in k order; its partial is
+# rounded to the row type (the type a transport would send); the source adds
+# the partials in ascending partition order.  Every sum is float32 from +0.0,
+# product and sum rounded separately.
+
+def _send_row(lay: Layout, t, r):
+    return lay.send_offset[r] + lay.token_slot[t, r]
+
+
+def send(lay: Layout, x: np.ndarray) -> np.ndarray:
+    """Source side of a staged dispatch: ``S[send_offset[r] + token_slot[t,r]] = x[t]``
+    for every partition r that hosts one of t's experts.  Returns ``S[N_send, H]``."""
+    x = np.asarray(x)
+    S = np.empty((lay.n_send, x.shape[1]), dtype=x.dtype)
+    t_idx, r_idx = np.nonzero(lay.is_token_in_rank)
+    S[_send_row(lay, t_idx, r_idx)] = x[t_idx]
+    return S
+
+
+def expand(lay: Layout, S: np.ndarray, dtype: str, topk_weights=None, scale_rows: bool = False):
+    """Receiver side of a staged dispatch: each send row goes to the receive
+    rows of its token's experts on that partition,
+    ``recv[recv_pos[t,k]] = S[send_offset[part] + token_slot[t,part]]`` with
+    ``part`` the partition of ``topk_idx[t,k]``; scaled as ``dispatch`` when
+    ``scale_rows``.  Returns ``(recv[R,H], recv_scores[R] or None)``."""
+    S = np.asarray(S)
+    T, K = lay.T, lay.K
+    recv = np.empty((lay.R, S.shape[1]), dtype=S.dtype)
+    rows = _send_row(lay, np.repeat(np.arange(T), K), lay.part.reshape(-1)).reshape(T, K)
+    if scale_rows:
+        if topk_weights is None:
+            raise ValueError("scale_rows needs topk_weights")
+        for k in range(K):
+            prod = np.asarray(topk_weights, np.float32)[:, k:k + 1] * to_f32(S[rows[:, k]], dtype)
+            recv[lay.recv_pos[:, k]] = from_f32(prod, dtype)
+    else:
+        for k in range(K):
+            recv[lay.recv_pos[:, k]] = S[rows[:, k]]
+    recv_scores = None
+    if topk_weights is not None:
+        recv_scores = np.empty(lay.R, dtype=np.float32)
+        recv_scores[lay.recv_pos.reshape(-1)] = np.asarray(topk_weights, np.float32).reshape(-1)
+    return recv, recv_scores
+
+
+def reduce_partitions(lay: Layout, y: np.ndarray, dtype: str, topk_weights=None) -> np.ndarray:
+    """Receiver side of a two-level combine: for every (token, partition) pair
+    the partial ``sum_k [w[t,k] *] y[recv_pos[t,k]]`` over the k whose expert
+    is on that partition, in k order, float32 from +0.0, rounded to the row
+    type.  Returns ``Q[N_send, H]`` in send-row order."""
+    yf = to_f32(y, dtype)
+    T, K = lay.T, lay.K
+    acc = np.zeros((lay.n_send, yf.shape[1]), dtype=np.float32)
+    t_all = np.arange(T)
+    for k in range(K):
+        rows = _send_row(lay, t_all, lay.part[:, k])      # each token's row for this k's partition
+        term = yf[lay.recv_pos[:, k]]
+        if topk_weights is not None:
+            term = np.asarray(topk_weights, np.float32)[:, k:k + 1] * term
+        # tokens are distinct within one k, so this is one add per send row
+        acc[rows] = acc[rows] + term
+    return from_f32(acc, dtype)
+
+
+def combine_partitions(lay: Layout, Q: np.ndarray, dtype: str) -> np.ndarray:
+    """Source side of a two-level combine: ``out[t] = round(sum_r f32(Q[send row
+    of (t,r)]))`` over t's partitions in ascending r, float32 from +0.0."""
+    Qf = to_f32(Q, dtype)
+    acc = np.zeros((lay.T, Qf.shape[1]), dtype=np.float32)
+    for r in range(lay.P):
+        ts = np.nonzero(lay.is_token_in_rank[:, r])[0]
+        acc[ts] = acc[ts] + Qf[_send_row(lay, ts, r)]
+    return from_f32(acc, dtype)
