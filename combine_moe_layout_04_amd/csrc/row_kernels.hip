@@ -82,10 +82,14 @@ __global__ __launch_bounds__(512) void scatter_kernel(ScatterArgs a) {
 
   const u32x4* src = static_cast<const u32x4*>(a.src) + (size_t)t * a.NV;
   u32x4* dst = static_cast<u32x4*>(a.dst);
+  // Lanes past the row end hold zeros: the scaled path converts every lane's
+  // chunk, and a conversion of an indeterminate value would let the
+  // compiler drop the j < NV guards.
   u32x4 v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int j = jb + c * kWave;
+    v[c] = u32x4{0u, 0u, 0u, 0u};
     if (j < a.NV) v[c] = src[j];
   }
   float f[CPL][SCALE ? V : 1];
@@ -227,6 +231,7 @@ __global__ __launch_bounds__(1024) void token_dot_kernel(DotArgs a) {
       for (int kk = 0; kk < KG; ++kk) {
         const int k = kg + kk;
         ok[kk] = false;
+        yv[kk] = u32x4{0u, 0u, 0u, 0u};
         if (k < a.K) {
           const int p = read_lane_i(q.pos, k);
           ok[kk] = (unsigned)p < (unsigned)a.R;
