@@ -92,13 +92,21 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
     Drop the low 16 bits after adding 0x7FFF plus the lowest kept bit, so that
     a discarded half rounds up only when the kept part is odd.  NaNs keep sign
     and top payload bits and are made quiet (bit 6 of the bf16 set).
+
+    The map is elementwise; it runs over slices of a bounded number of
+    elements only so that the 64-bit temporaries of a large array stay small.
     """
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    is_nan = (b & 0x7FFFFFFF) > 0x7F800000
-    keep_lsb = (b >> 16) & 1
-    rounded = (b + 0x7FFF + keep_lsb) >> 16
-    quiet_nan = (b >> 16) | 0x40
-    return np.where(is_nan, quiet_nan, rounded).astype(np.uint16)
+    flat = np.ascontiguousarray(x, dtype=np.float32).reshape(-1).view(np.uint32)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    step = 1 << 22
+    for i in range(0, flat.size, step):
+        b = flat[i:i + step].astype(np.uint64)
+        is_nan = (b & 0x7FFFFFFF) > 0x7F800000
+        keep_lsb = (b >> 16) & 1
+        rounded = (b + 0x7FFF + keep_lsb) >> 16
+        quiet_nan = (b >> 16) | 0x40
+        out[i:i + step] = np.where(is_nan, quiet_nan, rounded)
+    return out.reshape(np.shape(x))
 
 
 def to_f32(a: np.ndarray, dtype: str) -> np.ndarray:
