@@ -14,6 +14,11 @@ from .api import (  # noqa: F401
     moe_dispatch_bwd,
     moe_layout,
     moe_workspace_size,
+    moe_send_capacity,
+    moe_send,
+    moe_expand,
+    moe_reduce_partitions,
+    moe_combine_partitions,
 )
 from . import autograd  # noqa: F401
 

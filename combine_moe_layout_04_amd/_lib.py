@@ -34,6 +34,14 @@ SIGNATURES = {
                                 c_void_p, c_void_p, c_void_p]),
     "moe_dispatch_bwd": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p]),
+    "moe_send_capacity": (c_int, [c_void_p, ctypes.POINTER(c_int64)]),
+    "moe_send": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_void_p, c_int64, c_void_p]),
+    "moe_expand": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int64, c_void_p, c_int, c_void_p,
+                           c_void_p, c_void_p]),
+    "moe_reduce_partitions": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_void_p, c_void_p,
+                                      c_int64, c_void_p]),
+    "moe_combine_partitions": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int64, c_void_p,
+                                       c_void_p]),
     "moe_handle_field": (c_int, [c_void_p, c_int, ctypes.POINTER(c_void_p), ctypes.POINTER(c_size_t)]),
     "moe_handle_dims": (c_int, [c_void_p, ctypes.POINTER(c_int64), ctypes.POINTER(c_int),
                                 ctypes.POINTER(c_int), ctypes.POINTER(c_int)]),

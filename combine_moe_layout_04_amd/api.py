@@ -30,6 +30,7 @@ FIELDS = {  # name -> (id, dtype, shape as a function of (T,K,E,P))
     "recv_token": (8, torch.int32, lambda T, K, E, P: (T * K,)),
     "recv_k": (9, torch.int32, lambda T, K, E, P: (T * K,)),
     "status": (10, torch.int32, lambda T, K, E, P: (1,)),
+    "send_token": (11, torch.int32, lambda T, K, E, P: (T * min(K, P),)),
 }
 
 
@@ -208,6 +209,7 @@ def moe_combine_bwd(handle: Handle, grad_out: torch.Tensor, topk_weights: Option
                     grad_w=None):
     """grad_y[recv_pos[t,k]] = [w[t,k] *] grad_out[t]; grad_w[t,k] = <grad_out[t], y[row]>.
 
+    grad_y: None (allocate), False (rows not produced: grad_w only) or a tensor.
     grad_w: None (not produced), True (allocate) or a float32 [T,K] tensor.
     Returns (grad_y, grad_w or None)."""
     h = handle
@@ -224,7 +226,10 @@ def moe_combine_bwd(handle: Handle, grad_out: torch.Tensor, topk_weights: Option
         _need(y, "y", dev, (T * K, H), grad_out.dtype)
     if grad_y is None:
         grad_y = torch.empty((T * K, H), dtype=grad_out.dtype, device=dev)
-    _need(grad_y, "grad_y", dev, (T * K, H), grad_out.dtype)
+    elif grad_y is False:
+        grad_y = None  # router-weight gradient only
+    if grad_y is not None:
+        _need(grad_y, "grad_y", dev, (T * K, H), grad_out.dtype)
     if grad_w is True:
         grad_w = torch.empty((T, K), dtype=torch.float32, device=dev)
     elif grad_w is False:
@@ -242,6 +247,7 @@ def moe_dispatch_bwd(handle: Handle, grad_recv: torch.Tensor, topk_weights: Opti
     """grad_x[t] = sum_k [w[t,k] *] grad_recv[recv_pos[t,k]]; grad_s[t,k] = <grad_recv[row], x[t]>.
 
     Pass topk_weights iff the forward dispatch scaled its rows.
+    grad_x: None (allocate), False (rows not produced: grad_s only) or a tensor.
     grad_s: None, True (allocate) or a float32 [T,K] tensor.
     Returns (grad_x, grad_s or None)."""
     h = handle
@@ -258,7 +264,10 @@ def moe_dispatch_bwd(handle: Handle, grad_recv: torch.Tensor, topk_weights: Opti
         _need(x, "x", dev, (T, H), grad_recv.dtype)
     if grad_x is None:
         grad_x = torch.empty((T, H), dtype=grad_recv.dtype, device=dev)
-    _need(grad_x, "grad_x", dev, (T, H), grad_recv.dtype)
+    elif grad_x is False:
+        grad_x = None  # score gradient only
+    if grad_x is not None:
+        _need(grad_x, "grad_x", dev, (T, H), grad_recv.dtype)
     if grad_s is True:
         grad_s = torch.empty((T, K), dtype=torch.float32, device=dev)
     elif grad_s is False:
@@ -268,6 +277,92 @@ def moe_dispatch_bwd(handle: Handle, grad_recv: torch.Tensor, topk_weights: Opti
     _check(lib().moe_dispatch_bwd(h.ptr, _ptr(grad_recv), dt, H, _ptr(topk_weights), _ptr(x),
                                   _ptr(grad_x), _ptr(grad_s), _stream(dev)), "moe_dispatch_bwd")
     return grad_x, grad_s
+
+
+# ---- staged exchange ---------------------------------------------------------
+
+def moe_send_capacity(handle: Handle) -> int:
+    """Rows a send buffer must hold: T * min(K, P)."""
+    n = ctypes.c_int64(0)
+    _check(lib().moe_send_capacity(handle.ptr, ctypes.byref(n)), "moe_send_capacity")
+    return n.value
+
+
+def _send_buf(handle: Handle, t: Optional[torch.Tensor], H: int, dtype, name: str):
+    cap = moe_send_capacity(handle)
+    if t is None:
+        return torch.empty((cap, H), dtype=dtype, device=handle.device)
+    _need(t, name, handle.device, dtype=dtype)
+    if t.dim() != 2 or t.shape[1] != H or t.shape[0] < cap:
+        raise ValueError(f"{name} must be [>= {cap}, {H}]")
+    return t
+
+
+def moe_send(handle: Handle, x: torch.Tensor, send: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Source side of a staged dispatch: send[send_offset[r] + token_slot[t,r]] = x[t]."""
+    h = handle
+    _need(x, "x", h.device)
+    if x.dim() != 2 or x.shape[0] != h.T:
+        raise ValueError(f"x must be [{h.T}, H]")
+    H = x.shape[1]
+    send = _send_buf(h, send, H, x.dtype, "send")
+    _check(lib().moe_send(h.ptr, _ptr(x), _dtype_code(x), H, _ptr(send), send.shape[0],
+                          _stream(h.device)), "moe_send")
+    return send
+
+
+def moe_expand(handle: Handle, send: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+               scale_rows: bool = False, recv: Optional[torch.Tensor] = None, recv_scores=None):
+    """Receiver side of a staged dispatch; returns (recv, recv_scores or None)."""
+    h = handle
+    _need(send, "send", h.device)
+    H = send.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", h.device, (h.T, h.K), torch.float32)
+    if recv is None:
+        recv = torch.empty((h.T * h.K, H), dtype=send.dtype, device=h.device)
+    _need(recv, "recv", h.device, (h.T * h.K, H), send.dtype)
+    if recv_scores is True:
+        recv_scores = torch.empty(h.T * h.K, dtype=torch.float32, device=h.device)
+    elif recv_scores is False:
+        recv_scores = None
+    if recv_scores is not None:
+        _need(recv_scores, "recv_scores", h.device, (h.T * h.K,), torch.float32)
+    _check(lib().moe_expand(h.ptr, _ptr(send), _dtype_code(send), H, send.shape[0], _ptr(topk_weights),
+                            int(bool(scale_rows)), _ptr(recv), _ptr(recv_scores), _stream(h.device)),
+           "moe_expand")
+    return recv, recv_scores
+
+
+def moe_reduce_partitions(handle: Handle, y: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                          partial: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Receiver side of the two-level combine: one partial row per send row."""
+    h = handle
+    _need(y, "y", h.device)
+    if y.dim() != 2 or y.shape[0] != h.T * h.K:
+        raise ValueError(f"y must be [{h.T * h.K}, H]")
+    H = y.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", h.device, (h.T, h.K), torch.float32)
+    partial = _send_buf(h, partial, H, y.dtype, "partial")
+    _check(lib().moe_reduce_partitions(h.ptr, _ptr(y), _dtype_code(y), H, _ptr(topk_weights),
+                                       _ptr(partial), partial.shape[0], _stream(h.device)),
+           "moe_reduce_partitions")
+    return partial
+
+
+def moe_combine_partitions(handle: Handle, partial: torch.Tensor,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Source side of the two-level combine: partitions added in ascending order."""
+    h = handle
+    _need(partial, "partial", h.device)
+    H = partial.shape[1]
+    if out is None:
+        out = torch.empty((h.T, H), dtype=partial.dtype, device=h.device)
+    _need(out, "out", h.device, (h.T, H), partial.dtype)
+    _check(lib().moe_combine_partitions(h.ptr, _ptr(partial), _dtype_code(partial), H, partial.shape[0],
+                                        _ptr(out), _stream(h.device)), "moe_combine_partitions")
+    return out
 
 
 def moe_bench_copy(dst: torch.Tensor, src: torch.Tensor) -> None:

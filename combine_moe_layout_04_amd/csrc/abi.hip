@@ -62,6 +62,7 @@ WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs) {
   w.recv_pos = take((size_t)R * 4);
   w.recv_token = take((size_t)R * 4);
   w.recv_k = take((size_t)R * 4);
+  w.send_token = take((size_t)T * (K < P ? K : P) * 4);
   w.tok_mask = take((size_t)T * 8);
   w.hist = take((size_t)(E + 1 + P) * nblk * 4);
   w.total = o;
@@ -202,6 +203,7 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
   a.recv_pos = ws_ptr<int>(h, plan.recv_pos);
   a.recv_token = ws_ptr<int>(h, plan.recv_token);
   a.recv_k = ws_ptr<int>(h, plan.recv_k);
+  a.send_token = ws_ptr<int>(h, plan.send_token);
   a.status = ws_ptr<int>(h, plan.status);
   const int rc = hip_status(moe::launch_layout(a, stream));
   if (rc == MOE_OK) h->has_layout = true;
@@ -267,9 +269,10 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   if (st != MOE_OK) return st;
   if (grad_w && (!topk_weights || !y)) return MOE_ERR_INVALID_ARG;
   if (grad_w && (st = check_dot(h, NV)) != MOE_OK) return st;
+  if (!grad_y && !grad_w) return MOE_ERR_INVALID_ARG;
   if (h->T == 0) return MOE_OK;
-  if (!grad_out || !grad_y) return MOE_ERR_INVALID_ARG;
-  if (!aligned(grad_out, 16) || !aligned(grad_y, 16) || (grad_w && !aligned(y, 16)))
+  if (!grad_out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(grad_out, 16) || (grad_y && !aligned(grad_y, 16)) || (grad_w && !aligned(y, 16)))
     return MOE_ERR_ALIGNMENT;
   if ((topk_weights && !aligned(topk_weights, 4)) || (grad_w && !aligned(grad_w, 4)))
     return MOE_ERR_ALIGNMENT;
@@ -286,7 +289,7 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   a.dtype = dtype;
   a.scale = topk_weights != nullptr;
   a.status = ws_ptr<int>(h, h->plan.status);
-  st = hip_status(moe::launch_scatter(a, h->tune, stream));
+  st = grad_y ? hip_status(moe::launch_scatter(a, h->tune, stream)) : MOE_OK;
   if (st != MOE_OK || !grad_w) return st;
   // router-weight gradient: a separate pass over grad_out and y (measured
   // faster than fusing it into the row stores: HBM turns around less)
@@ -314,9 +317,10 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
   if (st != MOE_OK) return st;
   if (grad_s && (!topk_weights || !x)) return MOE_ERR_INVALID_ARG;
   if (grad_s && (st = check_dot(h, NV)) != MOE_OK) return st;
+  if (!grad_x && !grad_s) return MOE_ERR_INVALID_ARG;
   if (h->T == 0) return MOE_OK;
-  if (!grad_recv || !grad_x) return MOE_ERR_INVALID_ARG;
-  if (!aligned(grad_recv, 16) || !aligned(grad_x, 16) || (grad_s && !aligned(x, 16)))
+  if (!grad_recv) return MOE_ERR_INVALID_ARG;
+  if (!aligned(grad_recv, 16) || (grad_x && !aligned(grad_x, 16)) || (grad_s && !aligned(x, 16)))
     return MOE_ERR_ALIGNMENT;
   if ((topk_weights && !aligned(topk_weights, 4)) || (grad_s && !aligned(grad_s, 4)))
     return MOE_ERR_ALIGNMENT;
@@ -334,7 +338,7 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
     d.NV = NV;
     d.R = (int)(h->T * h->K);
     d.dtype = dtype;
-    d.gather = true;
+    d.gather = grad_x != nullptr;  // without grad_x: the score gradient only
     d.status = ws_ptr<int>(h, h->plan.status);
     return hip_status(moe::launch_token_dot(d, h->tune, stream));
   }
@@ -350,6 +354,110 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
   a.dtype = dtype;
   a.status = ws_ptr<int>(h, h->plan.status);
   return hip_status(moe::launch_gather(a, h->tune, stream));
+}
+
+int moe_send_capacity(moe_handle_t h, int64_t* rows) {
+  if (!valid_handle(h) || !rows) return MOE_ERR_INVALID_ARG;
+  if (!h->has_layout) return MOE_ERR_HANDLE;
+  *rows = h->T * (h->K < h->P ? h->K : h->P);
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the four staged calls; fills the arguments they share.
+int staged_args(const moe_handle_s* h, int dtype, int64_t H, int64_t send_rows, moe::StagedArgs* a) {
+  int NV = 0;
+  const int st = check_rows(h, dtype, H, &NV);
+  if (st != MOE_OK) return st;
+  const int64_t cap = h->T * (h->K < h->P ? h->K : h->P);
+  if (send_rows < cap) return MOE_ERR_SHAPE;
+  if (cap * (int64_t)((NV + 63) / 64) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  *a = moe::StagedArgs{};
+  a->recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
+  a->token_slot = ws_ptr<int>(h, h->plan.token_slot);
+  a->send_offset = ws_ptr<int>(h, h->plan.send_offset);
+  a->rank_offset = ws_ptr<int>(h, h->plan.rank_offset);
+  a->send_token = ws_ptr<int>(h, h->plan.send_token);
+  a->tok_mask = ws_ptr<unsigned long long>(h, h->plan.tok_mask);
+  a->T = (int)h->T;
+  a->K = h->K;
+  a->P = h->P;
+  a->NV = NV;
+  a->R = (int)(h->T * h->K);
+  a->send_cap = (int)cap;
+  a->dtype = dtype;
+  a->status = ws_ptr<int>(h, h->plan.status);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_send(moe_handle_t h, const void* x, int dtype, int64_t H, void* send, int64_t send_rows,
+             hipStream_t stream) {
+  moe::StagedArgs a;
+  const int st = staged_args(h, dtype, H, send_rows, &a);
+  if (st != MOE_OK) return st;
+  if (h->T == 0) return MOE_OK;
+  if (!x || !send) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(send, 16)) return MOE_ERR_ALIGNMENT;
+  a.src = x;
+  a.dst = send;
+  return hip_status(moe::launch_send(a, h->tune, stream));
+}
+
+int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t send_rows,
+               const float* topk_weights, int scale_rows, void* recv, float* recv_scores,
+               hipStream_t stream) {
+  moe::StagedArgs a;
+  const int st = staged_args(h, dtype, H, send_rows, &a);
+  if (st != MOE_OK) return st;
+  if (scale_rows != 0 && scale_rows != 1) return MOE_ERR_INVALID_ARG;
+  if ((scale_rows || recv_scores) && !topk_weights) return MOE_ERR_INVALID_ARG;
+  if (h->T == 0) return MOE_OK;
+  if (!send || !recv) return MOE_ERR_INVALID_ARG;
+  if (!aligned(send, 16) || !aligned(recv, 16)) return MOE_ERR_ALIGNMENT;
+  if ((topk_weights && !aligned(topk_weights, 4)) || (recv_scores && !aligned(recv_scores, 4)))
+    return MOE_ERR_ALIGNMENT;
+  a.src = send;
+  a.dst = recv;
+  a.w = topk_weights;
+  a.scores_out = recv_scores;
+  a.scale = scale_rows != 0;
+  return hip_status(moe::launch_expand(a, h->tune, stream));
+}
+
+int moe_reduce_partitions(moe_handle_t h, const void* y, int dtype, int64_t H,
+                          const float* topk_weights, void* partial, int64_t send_rows,
+                          hipStream_t stream) {
+  moe::StagedArgs a;
+  const int st = staged_args(h, dtype, H, send_rows, &a);
+  if (st != MOE_OK) return st;
+  if (h->T == 0) return MOE_OK;
+  if (!y || !partial) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(partial, 16)) return MOE_ERR_ALIGNMENT;
+  if (topk_weights && !aligned(topk_weights, 4)) return MOE_ERR_ALIGNMENT;
+  a.src = y;
+  a.dst = partial;
+  a.w = topk_weights;
+  return hip_status(moe::launch_reduce_partitions(a, h->tune, stream));
+}
+
+int moe_combine_partitions(moe_handle_t h, const void* partial, int dtype, int64_t H,
+                           int64_t send_rows, void* out, hipStream_t stream) {
+  moe::StagedArgs a;
+  const int st = staged_args(h, dtype, H, send_rows, &a);
+  if (st != MOE_OK) return st;
+  if (h->T == 0) return MOE_OK;
+  if (!partial || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(partial, 16) || !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
+  a.src = partial;
+  a.dst = out;
+  return hip_status(moe::launch_combine_partitions(a, h->tune, stream));
 }
 
 int moe_handle_field(moe_handle_t h, int field, void** dev_ptr, size_t* bytes) {
@@ -370,6 +478,7 @@ int moe_handle_field(moe_handle_t h, int field, void** dev_ptr, size_t* bytes) {
     case MOE_FIELD_RECV_TOKEN: off = p.recv_token; n = T * K * 4; break;
     case MOE_FIELD_RECV_K: off = p.recv_k; n = T * K * 4; break;
     case MOE_FIELD_STATUS: off = p.status; n = 4; break;
+    case MOE_FIELD_SEND_TOKEN: off = p.send_token; n = T * (K < P ? K : P) * 4; break;
     default: return MOE_ERR_INVALID_ARG;
   }
   *dev_ptr = h->ws + off;

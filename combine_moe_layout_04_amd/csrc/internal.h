@@ -13,7 +13,7 @@ constexpr int kLayoutThreads = 512;  // threads per layout workgroup
 struct WsLayout {
   size_t status, num_tokens_per_expert, num_tokens_per_rank, is_token_in_rank,
       expert_offset, rank_offset, send_offset, token_slot, recv_pos, recv_token,
-      recv_k, tok_mask, hist;
+      recv_k, send_token, tok_mask, hist;
   size_t total;
   int nblk;  // layout workgroups (token tiles)
   int tile;  // tokens per tile
@@ -39,6 +39,7 @@ struct LayoutArgs {
   int* recv_pos;
   int* recv_token;
   int* recv_k;
+  int* send_token;        // [T*min(K,P)] token of each send row
   int* status;
 };
 
@@ -89,6 +90,27 @@ struct DotArgs {
   int* status;
 };
 
+// Staged exchange: a deduplicated send buffer [send_cap, NV] per (token,
+// partition) pair, rows send_offset[r] + token_slot[t,r].
+struct StagedArgs {
+  const void* src;        // send: x [T]; expand: S [send_cap]; reduce: y [R]; combine: Q [send_cap]
+  void* dst;              // send: S; expand: recv [R]; reduce: Q; combine: out [T]
+  const int* recv_pos;    // [T, K]
+  const int* token_slot;  // [T, P]
+  const int* send_offset; // [P+1]
+  const int* rank_offset; // [P+1]
+  const int* send_token;  // [send_cap]
+  const unsigned long long* tok_mask;  // [T]
+  const float* w;         // [T, K] or null
+  float* scores_out;      // expand: [R] or null
+  int T, K, P, NV, R;
+  int send_cap;           // rows of the send buffer (>= send_offset[P])
+  int ngrp;               // wave groups per row (set by the launcher)
+  int dtype;
+  bool scale;             // expand: dst = round(w * src)
+  int* status;
+};
+
 struct Tuning {
   int chunks_per_lane;  // 1, 2, 4: consecutive 64-chunk segments per wave
   int nontemporal;      // 0, 1, 2
@@ -105,6 +127,10 @@ int64_t row_waves(int64_t T, int NV, int cpl);
 hipError_t launch_scatter(const ScatterArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_token_dot(const DotArgs& a, const Tuning& t, hipStream_t s);
+hipError_t launch_send(const StagedArgs& a, const Tuning& t, hipStream_t s);
+hipError_t launch_expand(const StagedArgs& a, const Tuning& t, hipStream_t s);
+hipError_t launch_reduce_partitions(const StagedArgs& a, const Tuning& t, hipStream_t s);
+hipError_t launch_combine_partitions(const StagedArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 
 }  // namespace moe

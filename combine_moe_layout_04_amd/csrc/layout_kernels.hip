@@ -14,7 +14,8 @@
 //          this one (one thread per (column, tile range), all its loads in
 //          flight), then one workgroup scan over the columns: every global
 //          offset and this tile's starts.  Token send slots come from
-//          per-partition ballots over the tile's tokens.  The tile's ids are
+//          per-partition ballots over the tile's tokens (with send_token,
+//          their inverse).  The tile's ids are
 //          staged in LDS; each wave ranks a contiguous span of pairs: wave64
 //          ballots match equal ids, a popcount over the lanes below gives
 //          the rank inside 64 pairs, and per-(wave, expert) cursors in LDS
@@ -263,7 +264,10 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
         const int on = (int)((m >> r) & 1ull);
         const uint64_t bal = __ballot(on);
         const int slot = base[E1 + r] - off[E1 + r] + __popcll(bal & lanes_below(lane));
-        if (lane < nt) a.token_slot[(size_t)(t0 + lane) * a.P + r] = on ? slot : -1;
+        if (lane < nt) {
+          a.token_slot[(size_t)(t0 + lane) * a.P + r] = on ? slot : -1;
+          if (on) a.send_token[off[E1 + r] - off[E1] + slot] = t0 + lane;
+        }
       }
     }
   } else {
@@ -292,7 +296,10 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
       const int on = (int)((m >> r) & 1ull);
       const uint64_t bal = __ballot(on);
       const int slot = wpre[wv * a.P + r] + __popcll(bal & lanes_below(lane));
-      if (tt < nt) a.token_slot[(size_t)(t0 + tt) * a.P + r] = on ? slot : -1;
+      if (tt < nt) {
+        a.token_slot[(size_t)(t0 + tt) * a.P + r] = on ? slot : -1;
+        if (on) a.send_token[off[E1 + r] - off[E1] + slot] = t0 + tt;
+      }
     }
     if (c0 + kLT < nt) {  // more rounds (very large tiles only): carry the counts
       for (int r = tid; r < a.P; r += kLT)

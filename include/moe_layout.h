@@ -86,7 +86,9 @@ enum moe_field {
   MOE_FIELD_RECV_POS              = 7, /* int32 [T,K] receive row of pair (t,k)            */
   MOE_FIELD_RECV_TOKEN            = 8, /* int32 [R]   token of each receive row            */
   MOE_FIELD_RECV_K                = 9, /* int32 [R]   k of each receive row                */
-  MOE_FIELD_STATUS                = 10 /* int32 [1]   device status bits                   */
+  MOE_FIELD_STATUS                = 10,/* int32 [1]   device status bits                   */
+  MOE_FIELD_SEND_TOKEN            = 11 /* int32 [T*min(K,P)] token of each send row
+                                          (rows >= send_offset[P] unspecified)          */
 };
 
 /* Optional launch knobs; zero means "library default".  A row is cut into
@@ -175,6 +177,9 @@ int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H,
  * takes partial 0; the result adds the segment values in order from +0.0.
  * Needs ceil(H*elem/1024) * K * 4 <= 65536 (else MOE_ERR_UNSUPPORTED).
  *   grad_out [T,H], y [R,H], grad_y [R,H] dtype; grad_w [T,K] float32.     */
+/* grad_y may be NULL when grad_w is given: then only the router-weight
+ * gradient is computed (the rows of a staged backward come from moe_send and
+ * moe_expand). */
 int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
                     const float* topk_weights, const void* y, void* grad_y,
                     float* grad_w, hipStream_t stream);
@@ -186,9 +191,63 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
  * differentiated straight through its rounding).  grad_s needs topk_weights
  * and x; same dot order and size limit as moe_combine_bwd.
  *   grad_recv [R,H], x [T,H], grad_x [T,H] dtype; grad_s [T,K] float32.   */
+/* grad_x may be NULL when grad_s is given: then only the score gradient is
+ * computed (the rows of a staged backward come from moe_reduce_partitions and
+ * moe_combine_partitions). */
 int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H,
                      const float* topk_weights, const void* x, void* grad_x,
                      float* grad_s, hipStream_t stream);
+
+/* ---- staged exchange ------------------------------------------------------
+ * The payload a cross-GPU transport moves, staged in one GPU's HBM: a send
+ * buffer with one row per (token, destination partition) pair, at row
+ * send_offset[r] + token_slot[t,r] ("Add an opt-in DeepEP transport for the
+ * AutoEP expert all-to-all", section "Why": a token is sent once per
+ * destination rank, not once per selected expert; arrivals are grouped by
+ * expert; the combine reduces back to token order).  send_offset[P] rows are
+ * used; buffers take a capacity of at least moe_send_capacity() rows, known
+ * on the host without a device sync.  Staged dispatch = moe_send +
+ * moe_expand (bitwise equal to moe_dispatch); staged combine =
+ * moe_reduce_partitions + moe_combine_partitions (its own summation order,
+ * below).  A staged backward uses the same calls: the combine's backward is
+ * moe_send + moe_expand of the output gradient (scaled), the dispatch's is
+ * moe_reduce_partitions + moe_combine_partitions of the receive-row gradient;
+ * the router-weight gradients come from moe_combine_bwd / moe_dispatch_bwd
+ * with NULL row outputs.
+ *
+ * Row pointers 16-byte aligned, dtype as in the other calls; send_rows is
+ * the caller's buffer capacity in rows (MOE_ERR_SHAPE if below
+ * moe_send_capacity()).                                                    */
+
+/* Rows a send buffer must hold: T * min(K, P), an upper bound of send_offset[P]. */
+int moe_send_capacity(moe_handle_t h, int64_t* rows);
+
+/* Source side: send[send_offset[r] + token_slot[t,r]] = x[t] for every
+ * partition r of token t (each x row is read once).  x [T,H].            */
+int moe_send(moe_handle_t h, const void* x, int dtype, int64_t H, void* send, int64_t send_rows,
+             hipStream_t stream);
+
+/* Receiver side: recv[recv_pos[t,k]] = send[send_offset[r] + token_slot[t,r]]
+ * for every pair whose expert is on partition r (each send row is read
+ * once); scale_rows and recv_scores as in moe_dispatch.  recv [T*K,H].    */
+int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t send_rows,
+               const float* topk_weights, int scale_rows, void* recv, float* recv_scores,
+               hipStream_t stream);
+
+/* Receiver side of the two-level combine: for every (token, partition) send
+ * row, partial = round(sum [w[t,k] *] y[recv_pos[t,k]]) over the token's k
+ * with an expert on that partition, in k order, float32 from +0.0 (product
+ * and sum rounded on their own); rounded to the row type, the type a
+ * transport sends.  y [T*K,H]; partial [send_rows,H]; weights may be NULL
+ * (plain sum).                                                             */
+int moe_reduce_partitions(moe_handle_t h, const void* y, int dtype, int64_t H,
+                          const float* topk_weights, void* partial, int64_t send_rows,
+                          hipStream_t stream);
+
+/* Source side: out[t] = round(sum of float32(partial[send row of (t,r)]))
+ * over t's partitions r in ascending order, float32 from +0.0.  out [T,H]. */
+int moe_combine_partitions(moe_handle_t h, const void* partial, int dtype, int64_t H,
+                           int64_t send_rows, void* out, hipStream_t stream);
 
 /* Device pointer and byte size of one handle field (no synchronisation). */
 int moe_handle_field(moe_handle_t h, int field, void** dev_ptr, size_t* bytes);
