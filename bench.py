@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--events", choices=["all", "dominant", "none"], default="dominant",
                     help="HIP events in the timed region: around every call, around the "
                          "dominant kernel's call only, or none")
+    ap.add_argument("--staged", action="store_true",
+                    help="staged exchange: send buffer per destination partition, receiver-side "
+                         "expansion, two-level combine")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph (no per-call events)")
     return ap.parse_args()
@@ -67,15 +70,18 @@ def parse():
 # The step: a list of calls, each with its algorithmic row bytes
 # --------------------------------------------------------------------------
 
-def step_calls(cfg):
+def step_calls(cfg, staged=False, n_send=None):
     """[(name, kind, pass, algorithmic row bytes)] of one step, in order.
 
     Row bytes only (index and weight traffic, about 4-12 bytes per (t,k)
     pair per call, are reported apart): TH = T*H*b token-row bytes, RH =
-    T*K*H*b receive-row bytes.
+    T*K*H*b receive-row bytes, NS = N_send*H*b send-buffer bytes (one row
+    per (token, destination partition) pair; n_send[p] for pass p).
     """
     TH = cfg.T * cfg.H * cfg.esize
     RH = cfg.R * cfg.H * cfg.esize
+    if staged:
+        return _staged_calls(cfg, TH, RH, [n * cfg.H * cfg.esize for n in n_send])
     if not cfg.absorbed:
         return [("layout", "layout", 0, 0),
                 ("dispatch", "dispatch", 0, TH + RH),
@@ -95,44 +101,98 @@ def step_calls(cfg):
     return calls
 
 
-def index_bytes(cfg):
+def _staged_calls(cfg, TH, RH, NS):
+    """The same step through the staged exchange: every dispatch is send +
+    expand, every combine is reduce_partitions + combine_partitions ("merge"),
+    and a router-side gradient is a row-free dot call of its own."""
+    if not cfg.absorbed:
+        n = NS[0]
+        return [("layout", "layout", 0, 0),
+                ("dispatch:send", "send_x", 0, TH + n),
+                ("dispatch:expand", "expand_x", 0, n + RH),
+                ("combine:reduce", "reduce_y_w", 0, RH + n),
+                ("combine:merge", "merge_out", 0, n + TH),
+                ("combine_bwd:send", "send_g", 0, TH + n),
+                ("combine_bwd:expand", "expand_g_w", 0, n + RH),
+                ("combine_bwd:dot", "dot_w", 0, TH + RH),
+                ("dispatch_bwd:reduce", "reduce_gr", 0, RH + n),
+                ("dispatch_bwd:merge", "merge_gx", 0, n + TH)]
+    calls = []
+    for p in range(3):
+        n = NS[p]
+        calls += [(f"layout.{p}", "layout", p, 0),
+                  (f"dispatch.{p}:send", "send_x", p, TH + n),
+                  (f"dispatch.{p}:expand", "expand_x_scaled", p, n + RH),
+                  (f"combine.{p}:reduce", "reduce_y", p, RH + n),
+                  (f"combine.{p}:merge", "merge_out", p, n + TH)]
+    for p in (0, 2):
+        n = NS[p]
+        calls += [(f"replay_layout.{p}", "layout", p, 0),
+                  (f"replay_dispatch.{p}:send", "send_x", p, TH + n),
+                  (f"replay_dispatch.{p}:expand", "expand_x_scaled", p, n + RH),
+                  (f"combine_bwd.{p}:send", "send_g", p, TH + n),
+                  (f"combine_bwd.{p}:expand", "expand_g", p, n + RH),
+                  (f"dispatch_bwd.{p}:reduce", "reduce_gr_w", p, RH + n),
+                  (f"dispatch_bwd.{p}:merge", "merge_gx", p, n + TH),
+                  (f"dispatch_bwd.{p}:dot", "dot_s", p, RH + TH)]
+    return calls
+
+
+def index_bytes(cfg, staged=False, n_send=None):
     """Index, weight and score traffic per step (reported apart from `value`)."""
     R, T = cfg.R, cfg.T
     per = {"layout": R * 4 * 2 + R * 4 * 3 + T * cfg.P * 5 + T * 8 * 2 + T * 8,
            "dispatch": R * 4 * 3, "dispatch_scaled": R * 4 * 3, "combine": R * 4 * 2,
            "combine_plain": R * 4, "combine_bwd": R * 4 * 3, "combine_bwd_plain": R * 4,
            "dispatch_bwd": R * 4, "dispatch_bwd_scaled": R * 4 * 3}
-    return sum(per[kind] for _, kind, _, _ in step_calls(cfg))
+    # staged calls: per token its partition mask and send slots; per pair its
+    # receive row, weight and score as used; per send row its token
+    tok = T * (8 + cfg.P * 4)
+    per.update(send_x=tok, send_g=tok, merge_out=tok, merge_gx=tok, dot_w=R * 4 * 3, dot_s=R * 4 * 3)
+    ns = max(n_send) * 4 if n_send else 0
+    for kind, words in (("expand_x", 3), ("expand_x_scaled", 3), ("expand_g", 1), ("expand_g_w", 2),
+                        ("reduce_y_w", 2), ("reduce_y", 1), ("reduce_gr", 1), ("reduce_gr_w", 2)):
+        per[kind] = R * 4 * words + ns
+    return sum(per[kind] for _, kind, _, _ in step_calls(cfg, staged, n_send))
 
 
-DOMINANT = "combine"  # the call whose kernel the roofline reports: the K-row gather-reduce
+# The call whose kernel the roofline reports: the K-row gather-reduce (in the
+# staged exchange, its receiver-side half).
+DOMINANT = {False: "combine", True: "combine:reduce"}
+KERNEL_SOURCES = {False: ("row_kernels.hip", "device_common.h"),
+                  True: ("staged_kernels.hip", "device_common.h")}
 
 
-def dominant_call(cfg):
-    return "combine" if not cfg.absorbed else "combine.0"
+def dominant_call(cfg, staged=False):
+    name = DOMINANT[staged]
+    if not cfg.absorbed:
+        return name
+    return name.replace("combine", "combine.0", 1)
 
 
-def kernel_source_hash():
-    """Hash of the sources of the row kernels (the counters' subject)."""
+def kernel_source_hash(staged=False):
+    """Hash of the sources of the dominant kernel (the counters' subject)."""
     h = hashlib.sha256()
-    for f in ("row_kernels.hip", "device_common.h"):
+    for f in KERNEL_SOURCES[staged]:
         with open(os.path.join(ROOT, "combine_moe_layout_04_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(cfg, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known size), or None
-    when the kernels have changed since the counters were taken."""
+def traffic_from_profiles(cfg, staged=False):
+    """HBM bytes per launch of the dominant call's kernel from the committed
+    counter summary (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known
+    size), or None when its sources have changed since the counters were
+    taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"^source_hash: (\w+)$", text, re.M)
-    if m is None or m.group(1) != kernel_source_hash():
+    call = DOMINANT[staged]
+    m = re.search(r"^source_hash\.%s: (\w+)$" % re.escape(call), text, re.M)
+    if m is None or m.group(1) != kernel_source_hash(staged):
         return None
-    m = re.search(r"^traffic_bytes_per_launch\.%s: (\d+)$" % re.escape(kernel), text, re.M)
+    m = re.search(r"^traffic_bytes_per_launch\.%s: (\d+)$" % re.escape(call), text, re.M)
     return None if m is None else int(m.group(1))
 
 
@@ -182,8 +242,8 @@ class HipEvents:
 # CPU baseline: the oracle, untuned, on a bounded sample of the same step
 # --------------------------------------------------------------------------
 
-def cpu_baseline(cfg, budget_s):
-    import numpy as np  # noqa: F401
+def cpu_baseline(cfg, budget_s, staged=False):
+    import numpy as np
 
     import workloads as W
     from oracle import moe_oracle as O
@@ -191,9 +251,11 @@ def cpu_baseline(cfg, budget_s):
     dt = cfg.dtype
     passes = 3 if cfg.absorbed else 1
     inps = [W.layer_inputs(cfg, seed=0, pss=p) for p in range(passes)]
-    calls = step_calls(cfg)
+    lays = [O.layout(inp.topk_idx, cfg.E, cfg.P) for inp in inps]
+    calls = step_calls(cfg, staged, [l.n_send for l in lays])
     step_b = sum(b for _, _, _, b in calls)
     lay = {}
+    st = {}  # staged: the last send buffer and partial rows of each pass
     n_calls, moved = 0, 0
     t0 = time.perf_counter()
     out_of_time = False
@@ -203,23 +265,40 @@ def cpu_baseline(cfg, budget_s):
             inp = inps[p]
             w = inp.topk_weights
             if kind == "layout":
-                lay[p] = O.layout(inp.topk_idx, cfg.E, cfg.P)
-            elif kind == "dispatch":
-                O.dispatch(lay[p], inp.x, dt, w)
+                lay[p] = L = O.layout(inp.topk_idx, cfg.E, cfg.P)
+            L = lay[p]
+            if kind == "dispatch":
+                O.dispatch(L, inp.x, dt, w)
             elif kind == "dispatch_scaled":
-                O.dispatch(lay[p], inp.x, dt, w, scale_rows=True)
+                O.dispatch(L, inp.x, dt, w, scale_rows=True)
             elif kind == "combine":
-                O.combine(lay[p], inp.y, dt, w)
+                O.combine(L, inp.y, dt, w)
             elif kind == "combine_plain":
-                O.combine(lay[p], inp.y, dt)
+                O.combine(L, inp.y, dt)
             elif kind == "combine_bwd":
-                O.combine_bwd(lay[p], inp.g, dt, w, inp.y)
+                O.combine_bwd(L, inp.g, dt, w, inp.y)
             elif kind == "combine_bwd_plain":
-                O.combine_bwd(lay[p], inp.g, dt)
+                O.combine_bwd(L, inp.g, dt)
             elif kind == "dispatch_bwd":
-                O.dispatch_bwd(lay[p], inp.grad_recv, dt)
+                O.dispatch_bwd(L, inp.grad_recv, dt)
             elif kind == "dispatch_bwd_scaled":
-                O.dispatch_bwd(lay[p], inp.grad_recv, dt, w, inp.x)
+                O.dispatch_bwd(L, inp.grad_recv, dt, w, inp.x)
+            elif kind in ("send_x", "send_g"):
+                st[p, "S"] = O.send(L, inp.x if kind == "send_x" else inp.g)
+            elif kind in ("expand_x", "expand_x_scaled", "expand_g", "expand_g_w"):
+                O.expand(L, st[p, "S"], dt, None if kind == "expand_g" else w,
+                         kind in ("expand_x_scaled", "expand_g_w"))
+            elif kind in ("reduce_y_w", "reduce_y", "reduce_gr", "reduce_gr_w"):
+                rows = inp.y if kind.startswith("reduce_y") else inp.grad_recv
+                st[p, "Q"] = O.reduce_partitions(L, rows, dt, w if kind.endswith("_w") else None)
+            elif kind in ("merge_out", "merge_gx"):
+                O.combine_partitions(L, st[p, "Q"], dt)
+            elif kind == "dot_w":
+                O.canonical_dot(np.repeat(inp.g, cfg.K, axis=0), inp.y[L.recv_pos.reshape(-1)], dt)
+            elif kind == "dot_s":
+                O.canonical_dot(inp.grad_recv[L.recv_pos.reshape(-1)], np.repeat(inp.x, cfg.K, axis=0), dt)
+            elif kind != "layout":
+                raise ValueError(kind)
             n_calls += 1
             moved += b
             if time.perf_counter() - t0 >= budget_s:
@@ -233,8 +312,8 @@ def cpu_baseline(cfg, budget_s):
         "cores": 1,
         "kind": "oracle",
         "sample": f"{done_steps} whole steps + {n_calls - done_steps * len(calls)} calls of the "
-                  f"{cfg.name} step (T={cfg.T}, H={cfg.H}, {dt}; {step_b / 1e6:.1f} MB of rows per step), "
-                  f"numpy single-threaded, {el:.1f} s",
+                  f"{cfg.name} {'staged ' if staged else ''}step (T={cfg.T}, H={cfg.H}, {dt}; "
+                  f"{step_b / 1e6:.1f} MB of rows per step), numpy single-threaded, {el:.1f} s",
     }
 
 
@@ -303,12 +382,34 @@ def main():
         s["grad_x"] = empty_rows(cfg.T)
         sets.append(s)
     del y0, g0, gr0, per_pass
+
+    n_send = None
+    if args.staged:
+        # Send buffers and partial rows.  A transport would carry each sent
+        # buffer (S_out, Q_out) into the peer's receive buffer (S_in, Q_in);
+        # cold, the receive buffers are separate ones, filled once here with
+        # valid rows and last touched a full buffer rotation ago; warm, they
+        # are the buffers just written.
+        n_send = []
+        for s in sets:
+            for p, q in enumerate(s["pass"]):
+                M.moe_layout(q["idx"], cfg.E, cfg.P, handle=q["h"], workspace=q["ws"])
+                cap = M.moe_send_capacity(q["h"])
+                q["S_out"], q["Q_out"] = empty_rows(cap), empty_rows(cap)
+                M.moe_send(q["h"], q["x"], send=q["S_out"])
+                M.moe_reduce_partitions(q["h"], s["y"], q["w"], partial=q["Q_out"])
+                if args.warm:
+                    q["S_in"], q["Q_in"] = q["S_out"], q["Q_out"]
+                else:
+                    q["S_in"], q["Q_in"] = q["S_out"].clone(), q["Q_out"].clone()
+                if s is sets[0]:
+                    n_send.append(int(q["h"].field("send_offset")[-1].item()))
     torch.cuda.synchronize()
 
-    calls = step_calls(cfg)
+    calls = step_calls(cfg, args.staged, n_send)
     names = [c[0] for c in calls]
     ncall = len(calls)
-    dom = dominant_call(cfg)
+    dom = dominant_call(cfg, args.staged)
 
     def run_call(s, kind, p):
         q = s["pass"][p]
@@ -333,6 +434,29 @@ def main():
         elif kind == "dispatch_bwd_scaled":
             gr = s["grad_y"] if args.warm else s["grad_recv"]
             M.moe_dispatch_bwd(h, gr, q["w"], q["x"], grad_x=s["grad_x"], grad_s=s["grad_w"])
+        # staged exchange
+        elif kind in ("send_x", "send_g"):
+            M.moe_send(h, q["x"] if kind == "send_x" else s["g"], send=q["S_out"])
+        elif kind in ("expand_x", "expand_x_scaled"):
+            M.moe_expand(h, q["S_in"], q["w"], scale_rows=kind == "expand_x_scaled",
+                         recv=q["recv"], recv_scores=q["scores"])
+        elif kind in ("expand_g", "expand_g_w"):
+            M.moe_expand(h, q["S_in"], q["w"] if kind == "expand_g_w" else None,
+                         scale_rows=kind == "expand_g_w", recv=s["grad_y"])
+        elif kind in ("reduce_y", "reduce_y_w"):
+            y = q["recv"] if args.warm else s["y"]
+            M.moe_reduce_partitions(h, y, q["w"] if kind == "reduce_y_w" else None, partial=q["Q_out"])
+        elif kind in ("reduce_gr", "reduce_gr_w"):
+            gr = s["grad_y"] if args.warm else s["grad_recv"]
+            M.moe_reduce_partitions(h, gr, q["w"] if kind == "reduce_gr_w" else None, partial=q["Q_out"])
+        elif kind in ("merge_out", "merge_gx"):
+            M.moe_combine_partitions(h, q["Q_in"], out=q["out"] if kind == "merge_out" else s["grad_x"])
+        elif kind == "dot_w":
+            yb = q["recv"] if args.warm else s["y_bwd"]
+            M.moe_combine_bwd(h, s["g"], q["w"], yb, grad_y=False, grad_w=s["grad_w"])
+        elif kind == "dot_s":
+            gr = s["grad_y"] if args.warm else s["grad_recv"]
+            M.moe_dispatch_bwd(h, gr, q["w"], q["x"], grad_x=False, grad_s=s["grad_w"])
         else:
             raise ValueError(kind)
 
@@ -412,12 +536,16 @@ def main():
     value = step_b / (ms_per_step * 1e-3) / 1e9
     dom_us = avg_us.get(dom)
     achieved = None if dom_us is None else row_bytes[dom] / (dom_us * 1e-6) / 1e9
-    traffic = traffic_from_profiles(cfg, DOMINANT)
+    traffic = traffic_from_profiles(cfg, args.staged)
+    direct_b = sum(b for _, _, _, b in step_calls(cfg))
 
     protocol = ("layout+dispatch+combine+combine_bwd+dispatch_bwd per step" if not cfg.absorbed else
                 "3 forward passes (layout, scaled dispatch, plain combine) + replay of layout and "
                 "dispatch and backward (combine_bwd copy, scaled dispatch_bwd with score gradient) "
                 "for passes 1 and 3, per step")
+    if args.staged:
+        protocol += ("; staged exchange: dispatch = send + expand, combine = reduce_partitions + "
+                     "combine_partitions, router-side gradients as row-free dot calls")
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -440,16 +568,29 @@ def main():
             "call_avg_us": {n: round(v, 2) for n, v in avg_us.items()},
             "call_median_us": {n: round(v, 2) for n, v in med_us.items()},
             "call_GBps": {n: round(row_bytes[n] / (avg_us[n] * 1e-6) / 1e9, 1) for n in avg_us if row_bytes[n]},
-            "index_bytes_per_step": index_bytes(cfg),
+            "index_bytes_per_step": index_bytes(cfg, args.staged, n_send),
             "host_enqueue_us_per_step": round(host_us, 1),
             "timing": ("hip graph replay" if graphs is not None else "eager launches") +
                       f", events: {args.events if graphs is None else 'none'}",
+            **({} if not args.staged else {
+                "exchange": "staged",
+                "n_send": n_send,
+                # rows a transport would move per exchange: one per (token,
+                # partition) pair here, one per (token, k) pair when direct
+                "exchange_bytes_per_step": sum(n_send[p] for _, kind, p, _ in calls
+                                               if kind.startswith(("send", "reduce"))) * cfg.H * cfg.esize,
+                "direct_exchange_bytes_per_step": sum(1 for _, kind, _, _ in calls
+                                                      if kind.startswith(("send", "reduce")))
+                                                  * cfg.R * cfg.H * cfg.esize,
+                "direct_step_bytes_per_s_GBps": round(direct_b / (ms_per_step * 1e-3) / 1e9, 2),
+            }),
             "tuning": {"chunks_per_lane": args.chunks_per_lane, "nontemporal": args.nontemporal,
                        "waves_per_block": args.waves_per_block, "layout_pairs": args.layout_pairs},
         },
         "roofline": None if achieved is None else {
             "bound": "hbm",
-            "kernel": f"{dom} (gather_kernel: K-row gather-reduce)",
+            "kernel": f"{dom} (" + ("reduce_partitions_kernel: per-partition K-row gather-reduce)"
+                                    if args.staged else "gather_kernel: K-row gather-reduce)"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -458,7 +599,7 @@ def main():
             "algorithmic_bytes_per_launch": row_bytes[dom],
             "avg_launch_us": round(dom_us, 2),
         },
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds),
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds, args.staged),
     }
     print(json.dumps(line), flush=True)
 

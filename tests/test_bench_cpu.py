@@ -1,0 +1,75 @@
+"""Host logic of bench.py: the byte accounting of a step, the one-GPU guard and
+the traffic-profile gating.  No GPU is used."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_direct_step_bytes_qwen3():
+    cfg = W.get_config("qwen3_30b_a3b")
+    TH = cfg.T * cfg.H * 2
+    RH = cfg.R * cfg.H * 2
+    total = sum(b for *_, b in bench.step_calls(cfg))
+    assert total == 4 * TH + 5 * RH == 738_197_504
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_30b_a3b", "deepseek_v3"])
+def test_staged_step_adds_the_send_buffer_traffic(name):
+    """Staged = direct + one more token-row read (the row-free dot re-reads g)
+    + 8 send-buffer passes (send, expand, reduce, merge; forward and backward)."""
+    cfg = W.get_config(name)
+    n_send = cfg.T * 2 + 5
+    TH = cfg.T * cfg.H * cfg.esize
+    NS = n_send * cfg.H * cfg.esize
+    direct = sum(b for *_, b in bench.step_calls(cfg))
+    staged = bench.step_calls(cfg, True, [n_send])
+    assert sum(b for *_, b in staged) == direct + TH + 8 * NS
+    assert bench.dominant_call(cfg, True) in [c[0] for c in staged]
+    kinds = [c[1] for c in staged]
+    assert kinds.count("send_x") == 1 and kinds.count("send_g") == 1 and kinds.count("dot_w") == 1
+
+
+def test_staged_absorbed_step_has_three_passes_and_two_backwards():
+    cfg = W.get_config("diffusion_gemma")
+    calls = bench.step_calls(cfg, True, [10, 20, 30])
+    names = [c[0] for c in calls]
+    assert names.count("layout.0") == 1 and "replay_layout.2" in names and "replay_layout.1" not in names
+    assert sum(1 for c in calls if c[1] == "dot_s") == 2
+    assert bench.dominant_call(cfg, True) == "combine.0:reduce"
+    NS = {p: n * cfg.H * cfg.esize for p, n in enumerate([10, 20, 30])}
+    for name, kind, p, b in calls:
+        if kind.startswith("send"):
+            assert b == cfg.T * cfg.H * cfg.esize + NS[p], name
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
+    cfg = W.get_config("qwen3_30b_a3b")
+    (tmp_path / "profiles").mkdir()
+    csrc = tmp_path / "combine_moe_layout_04_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in ("row_kernels.hip", "staged_kernels.hip", "device_common.h"):
+        (csrc / f).write_text(f"// {f}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    hd, hs = bench.kernel_source_hash(False), bench.kernel_source_hash(True)
+    (tmp_path / "profiles" / f"traffic_{cfg.name}.md").write_text(
+        f"source_hash.combine: {hd}\ntraffic_bytes_per_launch.combine: 123\n"
+        f"source_hash.combine:reduce: {hs}\ntraffic_bytes_per_launch.combine:reduce: 456\n")
+    assert bench.traffic_from_profiles(cfg) == 123
+    assert bench.traffic_from_profiles(cfg, True) == 456
+    (csrc / "staged_kernels.hip").write_text("// changed\n")
+    assert bench.traffic_from_profiles(cfg) == 123
+    assert bench.traffic_from_profiles(cfg, True) is None
