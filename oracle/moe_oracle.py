@@ -55,6 +55,8 @@ __all__ = [
     "to_f32",
     "from_f32",
     "recv_rows",
+    "recv_capacity",
+    "padded_count",
     "Layout",
     "layout",
     "dispatch",
@@ -134,12 +136,25 @@ def _elem_bytes(dtype: str) -> int:
 # --------------------------------------------------------------------------
 
 def recv_rows(T: int, K: int) -> int:
-    """Rows of the receive buffer: one per (token, k) pair.
+    """Receive rows that hold a pair: one per (token, k) pair.
 
     The torchtitan issue's "Motivation" sizes the routed-expert (W2) output
     as (T * top_k) x D, which is one row per routed pair.
     """
     return T * K
+
+
+def padded_count(n, m: int):
+    """Rows of an expert segment of n pairs padded to a multiple of m: the
+    least multiple of m that holds n (0 for an empty expert)."""
+    return (np.asarray(n, np.int64) + m - 1) // m * m
+
+
+def recv_capacity(T: int, K: int, E: int, pad_multiple: int = 1) -> int:
+    """Rows a receive buffer needs for any routing: T*K pairs, plus at most
+    m-1 padding rows per expert (each of the E segments is padded to a
+    multiple of m).  Known on the host before the layout runs."""
+    return T * K + E * (pad_multiple - 1)
 
 
 @dataclass
@@ -160,6 +175,7 @@ class Layout:
     recv_k: np.ndarray                 # [R]   int32, inverse map: k of a receive row
     part: np.ndarray                   # [T,K] int32, partition of pair (t,k)'s expert
     send_token: np.ndarray             # [N_send] int32, token of each send row
+    pad_multiple: int = 1              # expert segments padded to a multiple of this
 
     @property
     def n_send(self) -> int:
@@ -168,10 +184,18 @@ class Layout:
 
     @property
     def R(self) -> int:
-        return recv_rows(self.T, self.K)
+        """Rows of a receive buffer (T*K when unpadded)."""
+        return recv_capacity(self.T, self.K, self.E, self.pad_multiple)
+
+    def padding_rows(self) -> np.ndarray:
+        """Receive rows inside an expert's padded segment that hold no pair."""
+        n = self.num_tokens_per_expert.astype(np.int64)
+        lo = self.expert_offset[:-1].astype(np.int64) + n
+        hi = self.expert_offset[1:].astype(np.int64)
+        return np.concatenate([np.arange(a, b) for a, b in zip(lo, hi)] + [np.zeros(0, np.int64)])
 
 
-def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
+def layout(topk_idx: np.ndarray, E: int, P: int, pad_multiple: int = 1) -> Layout:
     """Dispatch layout of one routing decision.
 
     * Expert ``e`` lives on virtual partition ``e // (E/P)``: experts are split
@@ -195,6 +219,12 @@ def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
       the order the standard path's stable argsort gives, and it is a
       function of the routing alone, so a replay with the same routing
       reproduces every position.
+    * ``pad_multiple`` m (a handle constant; the DiffusionGemma dispatcher
+      page lists it as set once at construction): each expert's segment is
+      padded to ``padded_count(n_e, m)`` rows, so every ``expert_offset`` is
+      a multiple of m, as grouped-GEMM tiles want.  Pairs keep their order
+      and fill the front of their segment; the rest are padding rows, with
+      ``recv_token = recv_k = -1``.  m = 1 is the unpadded layout.
     """
     idx = np.asarray(topk_idx)
     if idx.ndim != 2:
@@ -206,6 +236,8 @@ def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
         raise ValueError("E must be a positive multiple of P")
     if T and (idx.min() < 0 or idx.max() >= E):
         raise ValueError("expert id out of range")
+    if pad_multiple < 1:
+        raise ValueError("pad_multiple must be >= 1")
     epr = E // P
     flat = idx.reshape(-1).astype(np.int64)
     R = recv_rows(T, K)
@@ -218,7 +250,7 @@ def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
     num_tokens_per_rank = is_token_in_rank.sum(axis=0, dtype=np.int64).astype(np.int32)
 
     expert_offset = np.zeros(E + 1, dtype=np.int64)
-    expert_offset[1:] = np.cumsum(num_tokens_per_expert)
+    expert_offset[1:] = np.cumsum(padded_count(num_tokens_per_expert, pad_multiple))
     rank_offset = expert_offset[np.arange(P + 1) * epr]
     send_offset = np.zeros(P + 1, dtype=np.int64)
     send_offset[1:] = np.cumsum(num_tokens_per_rank)
@@ -230,10 +262,18 @@ def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
                                 + [np.zeros(0, np.int64)])
 
     order = np.argsort(flat, kind="stable")                  # pair ids, expert-major
+    # rank of each pair among its expert's pairs, then its expert's first row
+    first_pair = np.zeros(E + 1, dtype=np.int64)
+    first_pair[1:] = np.cumsum(num_tokens_per_expert)
+    e_sorted = flat[order]
+    pos_sorted = expert_offset[e_sorted] + (np.arange(R) - first_pair[e_sorted])
     recv_pos = np.empty(R, dtype=np.int64)
-    recv_pos[order] = np.arange(R)
-    recv_token = order // K
-    recv_k = order % K
+    recv_pos[order] = pos_sorted
+    cap = recv_capacity(T, K, E, pad_multiple)
+    recv_token = np.full(cap, -1, dtype=np.int64)
+    recv_k = np.full(cap, -1, dtype=np.int64)
+    recv_token[pos_sorted] = order // K
+    recv_k[pos_sorted] = order % K
 
     i32 = lambda a: np.ascontiguousarray(a, dtype=np.int32)
     return Layout(
@@ -250,6 +290,7 @@ def layout(topk_idx: np.ndarray, E: int, P: int) -> Layout:
         recv_k=i32(recv_k),
         part=i32(part),
         send_token=i32(send_token),
+        pad_multiple=int(pad_multiple),
     )
 
 
@@ -269,11 +310,16 @@ def dispatch(lay: Layout, x: np.ndarray, dtype: str, topk_weights=None,
     * ``scale_rows``: the scores are absorbed before W2.  The row is scaled in
       float32 and cast back, ``recv = bf16(f32(x[t]) * w[t,k])``.  On one GPU,
       with no expert GEMM, the dispatch output is where that scaling lands.
+    * Padded layouts: the padding rows of every expert segment are zero rows
+      with a zero score (the zero-sentinel scores of the DiffusionGemma
+      dispatcher page's padded permute).  Rows past ``expert_offset[E]`` are
+      left unwritten.
     """
     x = np.asarray(x)
     T, K = lay.T, lay.K
     H = x.shape[1]
     recv = np.empty((lay.R, H), dtype=x.dtype)
+    recv[lay.padding_rows()] = 0
     recv_scores = None
     if scale_rows:
         if topk_weights is None:
@@ -287,6 +333,7 @@ def dispatch(lay: Layout, x: np.ndarray, dtype: str, topk_weights=None,
             recv[lay.recv_pos[:, k]] = x
     if topk_weights is not None:
         recv_scores = np.empty(lay.R, dtype=np.float32)
+        recv_scores[lay.padding_rows()] = 0.0
         recv_scores[lay.recv_pos.reshape(-1)] = np.asarray(topk_weights, np.float32).reshape(-1)
     return recv, recv_scores
 
@@ -324,6 +371,7 @@ def combine_bwd(lay: Layout, grad_out: np.ndarray, dtype: str, topk_weights=None
     g = np.asarray(grad_out)
     T, K = lay.T, lay.K
     grad_y = np.empty((lay.R, g.shape[1]), dtype=g.dtype)
+    grad_y[lay.padding_rows()] = 0      # padding rows get no gradient
     if topk_weights is None:
         for k in range(K):
             grad_y[lay.recv_pos[:, k]] = g
@@ -446,6 +494,7 @@ def expand(lay: Layout, S: np.ndarray, dtype: str, topk_weights=None, scale_rows
     S = np.asarray(S)
     T, K = lay.T, lay.K
     recv = np.empty((lay.R, S.shape[1]), dtype=S.dtype)
+    recv[lay.padding_rows()] = 0
     rows = _send_row(lay, np.repeat(np.arange(T), K), lay.part.reshape(-1)).reshape(T, K)
     if scale_rows:
         if topk_weights is None:
@@ -459,6 +508,7 @@ def expand(lay: Layout, S: np.ndarray, dtype: str, topk_weights=None, scale_rows
     recv_scores = None
     if topk_weights is not None:
         recv_scores = np.empty(lay.R, dtype=np.float32)
+        recv_scores[lay.padding_rows()] = 0.0
         recv_scores[lay.recv_pos.reshape(-1)] = np.asarray(topk_weights, np.float32).reshape(-1)
     return recv, recv_scores
 
