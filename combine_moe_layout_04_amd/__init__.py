@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     moe_layout,
     moe_workspace_size,
     moe_send_capacity,
+    moe_recv_capacity,
     moe_send,
     moe_expand,
     moe_reduce_partitions,

@@ -24,6 +24,9 @@ class MoeTuning(ctypes.Structure):
 SIGNATURES = {
     "moe_workspace_size": (c_int, [c_int64, c_int, c_int, c_int, ctypes.POINTER(c_size_t)]),
     "moe_handle_create": (c_int, [ctypes.POINTER(c_void_p), ctypes.POINTER(MoeTuning)]),
+    "moe_workspace_size_padded": (c_int, [c_int64, c_int, c_int, c_int, c_int, ctypes.POINTER(c_size_t)]),
+    "moe_handle_create_padded": (c_int, [ctypes.POINTER(c_void_p), ctypes.POINTER(MoeTuning), c_int]),
+    "moe_recv_capacity": (c_int, [c_void_p, ctypes.POINTER(c_int64)]),
     "moe_handle_destroy": (c_int, [c_void_p]),
     "moe_layout": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int, c_int, c_int, c_void_p,
                            c_size_t, c_void_p]),

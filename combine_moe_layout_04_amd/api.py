@@ -18,19 +18,19 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_I32, MOE_I64 = 0, 1
 STATUS_BAD_EXPERT, STATUS_BAD_POSITION = 1, 2
 
-FIELDS = {  # name -> (id, dtype, shape as a function of (T,K,E,P))
-    "num_tokens_per_expert": (0, torch.int32, lambda T, K, E, P: (E,)),
-    "num_tokens_per_rank": (1, torch.int32, lambda T, K, E, P: (P,)),
-    "is_token_in_rank": (2, torch.uint8, lambda T, K, E, P: (T, P)),
-    "expert_offset": (3, torch.int32, lambda T, K, E, P: (E + 1,)),
-    "rank_offset": (4, torch.int32, lambda T, K, E, P: (P + 1,)),
-    "send_offset": (5, torch.int32, lambda T, K, E, P: (P + 1,)),
-    "token_slot": (6, torch.int32, lambda T, K, E, P: (T, P)),
-    "recv_pos": (7, torch.int32, lambda T, K, E, P: (T, K)),
-    "recv_token": (8, torch.int32, lambda T, K, E, P: (T * K,)),
-    "recv_k": (9, torch.int32, lambda T, K, E, P: (T * K,)),
-    "status": (10, torch.int32, lambda T, K, E, P: (1,)),
-    "send_token": (11, torch.int32, lambda T, K, E, P: (T * min(K, P),)),
+FIELDS = {  # name -> (id, dtype, shape as a function of (T,K,E,P,R))
+    "num_tokens_per_expert": (0, torch.int32, lambda T, K, E, P, R: (E,)),
+    "num_tokens_per_rank": (1, torch.int32, lambda T, K, E, P, R: (P,)),
+    "is_token_in_rank": (2, torch.uint8, lambda T, K, E, P, R: (T, P)),
+    "expert_offset": (3, torch.int32, lambda T, K, E, P, R: (E + 1,)),
+    "rank_offset": (4, torch.int32, lambda T, K, E, P, R: (P + 1,)),
+    "send_offset": (5, torch.int32, lambda T, K, E, P, R: (P + 1,)),
+    "token_slot": (6, torch.int32, lambda T, K, E, P, R: (T, P)),
+    "recv_pos": (7, torch.int32, lambda T, K, E, P, R: (T, K)),
+    "recv_token": (8, torch.int32, lambda T, K, E, P, R: (R,)),
+    "recv_k": (9, torch.int32, lambda T, K, E, P, R: (R,)),
+    "status": (10, torch.int32, lambda T, K, E, P, R: (1,)),
+    "send_token": (11, torch.int32, lambda T, K, E, P, R: (T * min(K, P),)),
 }
 
 
@@ -73,9 +73,10 @@ def _need(t: torch.Tensor, name: str, device, shape=None, dtype=None):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
-def moe_workspace_size(T: int, K: int, E: int, P: int) -> int:
+def moe_workspace_size(T: int, K: int, E: int, P: int, pad_multiple: int = 1) -> int:
     n = ctypes.c_size_t(0)
-    _check(lib().moe_workspace_size(T, K, E, P, ctypes.byref(n)), "moe_workspace_size")
+    _check(lib().moe_workspace_size_padded(T, K, E, P, pad_multiple, ctypes.byref(n)),
+           "moe_workspace_size")
     return n.value
 
 
@@ -83,13 +84,15 @@ class Handle:
     """Opaque layout handle plus the device workspace its arrays live in."""
 
     def __init__(self, chunks_per_lane: int = 0, nontemporal: int = 1, waves_per_block: int = 0,
-                 layout_pairs: int = 0):
+                 layout_pairs: int = 0, pad_multiple: int = 1):
         tun = MoeTuning(chunks_per_lane, nontemporal, waves_per_block, layout_pairs)
         h = ctypes.c_void_p()
-        _check(lib().moe_handle_create(ctypes.byref(h), ctypes.byref(tun)), "moe_handle_create")
+        _check(lib().moe_handle_create_padded(ctypes.byref(h), ctypes.byref(tun), int(pad_multiple)),
+               "moe_handle_create")
         self._h = h
+        self.pad_multiple = int(pad_multiple)  # fixed for the handle's life
         self.workspace: Optional[torch.Tensor] = None
-        self.T = self.K = self.E = self.P = None
+        self.T = self.K = self.E = self.P = self.R = None
         self.device = None
 
     def __del__(self):
@@ -113,7 +116,7 @@ class Handle:
         _check(lib().moe_handle_field(self._h, fid, ctypes.byref(p), ctypes.byref(n)), "moe_handle_field")
         off = (p.value or 0) - self.workspace.data_ptr()
         raw = self.workspace[off:off + n.value]
-        return raw.view(dt).reshape(shape(self.T, self.K, self.E, self.P))
+        return raw.view(dt).reshape(shape(self.T, self.K, self.E, self.P, self.R))
 
     def check(self) -> int:
         """Synchronises the current stream and returns the device status bits."""
@@ -137,8 +140,8 @@ def moe_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
         raise TypeError("topk_idx must be int32 or int64")
     T, K = topk_idx.shape
     E, P = int(num_experts), int(num_partitions)
-    need = moe_workspace_size(T, K, E, P)
     h = handle if handle is not None else Handle()
+    need = moe_workspace_size(T, K, E, P, h.pad_multiple)
     if workspace is None:
         ws = h.workspace
         if ws is None or ws.numel() < need or ws.device != dev:
@@ -149,7 +152,15 @@ def moe_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
     _check(lib().moe_layout(h.ptr, _ptr(topk_idx), itype, T, K, E, P, _ptr(ws), ws.numel(),
                             _stream(dev)), "moe_layout")
     h.workspace, h.T, h.K, h.E, h.P, h.device = ws, T, K, E, P, dev
+    n = ctypes.c_int64(0)
+    _check(lib().moe_recv_capacity(h.ptr, ctypes.byref(n)), "moe_recv_capacity")
+    h.R = n.value  # receive rows: T*K, plus the padding capacity of a padded handle
     return h
+
+
+def moe_recv_capacity(handle: Handle) -> int:
+    """Rows of a receive buffer for the handle's layout: T*K + E*(pad_multiple-1)."""
+    return handle.R
 
 
 def moe_dispatch(handle: Handle, x: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
@@ -169,15 +180,16 @@ def moe_dispatch(handle: Handle, x: torch.Tensor, topk_weights: Optional[torch.T
     dt = _dtype_code(x)
     if topk_weights is not None:
         _need(topk_weights, "topk_weights", dev, (T, K), torch.float32)
+    R = h.R
     if recv is None:
-        recv = torch.empty((T * K, H), dtype=x.dtype, device=dev)
-    _need(recv, "recv", dev, (T * K, H), x.dtype)
+        recv = torch.empty((R, H), dtype=x.dtype, device=dev)
+    _need(recv, "recv", dev, (R, H), x.dtype)
     if recv_scores is True:
-        recv_scores = torch.empty(T * K, dtype=torch.float32, device=dev)
+        recv_scores = torch.empty(R, dtype=torch.float32, device=dev)
     elif recv_scores is False:
         recv_scores = None
     if recv_scores is not None:
-        _need(recv_scores, "recv_scores", dev, (T * K,), torch.float32)
+        _need(recv_scores, "recv_scores", dev, (R,), torch.float32)
     _check(lib().moe_dispatch(h.ptr, _ptr(x), dt, H, _ptr(topk_weights), int(bool(scale_rows)),
                               _ptr(recv), _ptr(recv_scores), _stream(dev)), "moe_dispatch")
     return recv, recv_scores
@@ -190,8 +202,8 @@ def moe_combine(handle: Handle, y: torch.Tensor, topk_weights: Optional[torch.Te
     dev = h.device
     T, K = h.T, h.K
     _need(y, "y", dev)
-    if y.dim() != 2 or y.shape[0] != T * K:
-        raise ValueError(f"y must be [{T * K}, H]")
+    if y.dim() != 2 or y.shape[0] != h.R:
+        raise ValueError(f"y must be [{h.R}, H]")
     H = y.shape[1]
     dt = _dtype_code(y)
     if topk_weights is not None:
@@ -223,13 +235,13 @@ def moe_combine_bwd(handle: Handle, grad_out: torch.Tensor, topk_weights: Option
     if topk_weights is not None:
         _need(topk_weights, "topk_weights", dev, (T, K), torch.float32)
     if y is not None:
-        _need(y, "y", dev, (T * K, H), grad_out.dtype)
+        _need(y, "y", dev, (h.R, H), grad_out.dtype)
     if grad_y is None:
-        grad_y = torch.empty((T * K, H), dtype=grad_out.dtype, device=dev)
+        grad_y = torch.empty((h.R, H), dtype=grad_out.dtype, device=dev)
     elif grad_y is False:
         grad_y = None  # router-weight gradient only
     if grad_y is not None:
-        _need(grad_y, "grad_y", dev, (T * K, H), grad_out.dtype)
+        _need(grad_y, "grad_y", dev, (h.R, H), grad_out.dtype)
     if grad_w is True:
         grad_w = torch.empty((T, K), dtype=torch.float32, device=dev)
     elif grad_w is False:
@@ -254,8 +266,8 @@ def moe_dispatch_bwd(handle: Handle, grad_recv: torch.Tensor, topk_weights: Opti
     dev = h.device
     T, K = h.T, h.K
     _need(grad_recv, "grad_recv", dev)
-    if grad_recv.dim() != 2 or grad_recv.shape[0] != T * K:
-        raise ValueError(f"grad_recv must be [{T * K}, H]")
+    if grad_recv.dim() != 2 or grad_recv.shape[0] != h.R:
+        raise ValueError(f"grad_recv must be [{h.R}, H]")
     H = grad_recv.shape[1]
     dt = _dtype_code(grad_recv)
     if topk_weights is not None:
@@ -320,14 +332,14 @@ def moe_expand(handle: Handle, send: torch.Tensor, topk_weights: Optional[torch.
     if topk_weights is not None:
         _need(topk_weights, "topk_weights", h.device, (h.T, h.K), torch.float32)
     if recv is None:
-        recv = torch.empty((h.T * h.K, H), dtype=send.dtype, device=h.device)
-    _need(recv, "recv", h.device, (h.T * h.K, H), send.dtype)
+        recv = torch.empty((h.R, H), dtype=send.dtype, device=h.device)
+    _need(recv, "recv", h.device, (h.R, H), send.dtype)
     if recv_scores is True:
-        recv_scores = torch.empty(h.T * h.K, dtype=torch.float32, device=h.device)
+        recv_scores = torch.empty(h.R, dtype=torch.float32, device=h.device)
     elif recv_scores is False:
         recv_scores = None
     if recv_scores is not None:
-        _need(recv_scores, "recv_scores", h.device, (h.T * h.K,), torch.float32)
+        _need(recv_scores, "recv_scores", h.device, (h.R,), torch.float32)
     _check(lib().moe_expand(h.ptr, _ptr(send), _dtype_code(send), H, send.shape[0], _ptr(topk_weights),
                             int(bool(scale_rows)), _ptr(recv), _ptr(recv_scores), _stream(h.device)),
            "moe_expand")
@@ -339,8 +351,8 @@ def moe_reduce_partitions(handle: Handle, y: torch.Tensor, topk_weights: Optiona
     """Receiver side of the two-level combine: one partial row per send row."""
     h = handle
     _need(y, "y", h.device)
-    if y.dim() != 2 or y.shape[0] != h.T * h.K:
-        raise ValueError(f"y must be [{h.T * h.K}, H]")
+    if y.dim() != 2 or y.shape[0] != h.R:
+        raise ValueError(f"y must be [{h.R}, H]")
     H = y.shape[1]
     if topk_weights is not None:
         _need(topk_weights, "topk_weights", h.device, (h.T, h.K), torch.float32)

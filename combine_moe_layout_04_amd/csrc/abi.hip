@@ -12,6 +12,8 @@ struct moe_handle_s {
   bool has_layout = false;
   int64_t T = 0;
   int K = 0, E = 0, P = 0;
+  int pad = 1;     // expert segments padded to a multiple of this (fixed at creation)
+  int64_t R = 0;   // receive rows of the current layout: T*K + E*(pad-1)
   char* ws = nullptr;
   moe::WsLayout plan{};
   moe::Tuning tune{};
@@ -21,7 +23,7 @@ namespace moe {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs) {
+WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs, int pad) {
   WsLayout w{};
   // Token tiles of the layout: at most layout_pairs (t,k) pairs per tile
   // (512: one per thread of a layout workgroup), unless that needs more
@@ -59,9 +61,10 @@ WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs) {
   w.send_offset = take((size_t)(P + 1) * 4);
   w.is_token_in_rank = take((size_t)T * P);
   w.token_slot = take((size_t)T * P * 4);
+  const int64_t cap = recv_capacity(T, K, E, pad);  // the inverse maps have a row per receive row
   w.recv_pos = take((size_t)R * 4);
-  w.recv_token = take((size_t)R * 4);
-  w.recv_k = take((size_t)R * 4);
+  w.recv_token = take((size_t)cap * 4);
+  w.recv_k = take((size_t)cap * 4);
   w.send_token = take((size_t)T * (K < P ? K : P) * 4);
   w.tok_mask = take((size_t)T * 8);
   w.hist = take((size_t)(E + 1 + P) * nblk * 4);
@@ -88,6 +91,12 @@ int check_shape(int64_t T, int K, int E, int P) {
   return MOE_OK;
 }
 
+int check_pad(int64_t T, int K, int E, int pad) {
+  if (pad < 1 || pad > moe::kMaxPadMultiple) return MOE_ERR_INVALID_ARG;
+  if (moe::recv_capacity(T, K, E, pad) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 // Shared checks of the four row calls.  Returns MOE_OK and NV (16-byte chunks
 // per row), or an error.
 int check_rows(const moe_handle_s* h, int dtype, int64_t H, int* NV) {
@@ -97,7 +106,7 @@ int check_rows(const moe_handle_s* h, int dtype, int64_t H, int* NV) {
   if (eb == 0) return MOE_ERR_UNSUPPORTED;
   if (H < 1 || (H * eb) % 16 != 0) return MOE_ERR_SHAPE;
   const int64_t nv = H * eb / 16;
-  if (nv >= (int64_t(1) << 31) || nv * h->T * h->K >= (int64_t(1) << 62)) return MOE_ERR_UNSUPPORTED;
+  if (nv >= (int64_t(1) << 31) || nv * h->R >= (int64_t(1) << 62)) return MOE_ERR_UNSUPPORTED;
   // one wave per (token, segment): the grid must fit in a 32-bit wave index
   if (moe::row_waves(h->T, (int)nv, 1) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   *NV = (int)nv;
@@ -116,20 +125,45 @@ T* ws_ptr(const moe_handle_s* h, size_t off) {
   return reinterpret_cast<T*>(h->ws + off);
 }
 
+// Padded layouts: zero rows (and zero scores) in the padding of every expert
+// segment of a receive buffer the call just wrote.  Nothing when unpadded.
+int fill_padding(const moe_handle_s* h, void* rows, float* scores, int NV, hipStream_t stream) {
+  if (h->pad <= 1) return MOE_OK;
+  moe::PadArgs p{};
+  p.dst = rows;
+  p.scores_out = scores;
+  p.expert_offset = ws_ptr<int>(h, h->plan.expert_offset);
+  p.num_tokens_per_expert = ws_ptr<int>(h, h->plan.num_tokens_per_expert);
+  p.E = h->E;
+  p.NV = NV;
+  p.R = (int)h->R;
+  return hip_status(moe::launch_pad_fill(p, h->tune, stream));
+}
+
 }  // namespace
 
 extern "C" {
 
-int moe_workspace_size(int64_t T, int K, int E, int P, size_t* bytes) {
+int moe_workspace_size_padded(int64_t T, int K, int E, int P, int pad_multiple, size_t* bytes) {
   if (!bytes) return MOE_ERR_INVALID_ARG;
-  const int st = check_shape(T, K, E, P);
+  int st = check_shape(T, K, E, P);
   if (st != MOE_OK) return st;
-  *bytes = moe::plan_workspace(T, K, E, P).total;
+  if ((st = check_pad(T, K, E, pad_multiple)) != MOE_OK) return st;
+  *bytes = moe::plan_workspace(T, K, E, P, moe::kLayoutThreads, pad_multiple).total;
   return MOE_OK;
 }
 
+int moe_workspace_size(int64_t T, int K, int E, int P, size_t* bytes) {
+  return moe_workspace_size_padded(T, K, E, P, 1, bytes);
+}
+
 int moe_handle_create(moe_handle_t* out, const moe_tuning* tuning) {
+  return moe_handle_create_padded(out, tuning, 1);
+}
+
+int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pad_multiple) {
   if (!out) return MOE_ERR_INVALID_ARG;
+  if (pad_multiple < 1 || pad_multiple > moe::kMaxPadMultiple) return MOE_ERR_INVALID_ARG;
   // defaults: one segment per wave, non-temporal receive rows, 4 waves per
   // workgroup, 512-pair layout tiles
   moe::Tuning t{1, 1, 4, moe::kLayoutThreads};
@@ -148,6 +182,7 @@ int moe_handle_create(moe_handle_t* out, const moe_tuning* tuning) {
   moe_handle_s* h = new (std::nothrow) moe_handle_s();
   if (!h) return MOE_ERR_INVALID_ARG;
   h->tune = t;
+  h->pad = pad_multiple;
   *out = h;
   return MOE_OK;
 }
@@ -162,22 +197,25 @@ int moe_handle_destroy(moe_handle_t h) {
 int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K, int E,
                int P, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!valid_handle(h)) return MOE_ERR_INVALID_ARG;
-  const int st = check_shape(T, K, E, P);
+  int st = check_shape(T, K, E, P);
   if (st != MOE_OK) return st;
+  if ((st = check_pad(T, K, E, h->pad)) != MOE_OK) return st;
   if (itype != MOE_I32 && itype != MOE_I64) return MOE_ERR_UNSUPPORTED;
   if (!workspace || (T > 0 && !topk_idx)) return MOE_ERR_INVALID_ARG;
   if (!aligned(workspace, 256)) return MOE_ERR_ALIGNMENT;
   if (T > 0 && !aligned(topk_idx, itype == MOE_I32 ? 4 : 8)) return MOE_ERR_ALIGNMENT;
-  if (workspace_bytes < moe::plan_workspace(T, K, E, P).total) return MOE_ERR_WORKSPACE;
+  const moe::WsLayout sized = moe::plan_workspace(T, K, E, P, moe::kLayoutThreads, h->pad);
+  if (workspace_bytes < sized.total) return MOE_ERR_WORKSPACE;
   // the handle's tile size: never more tiles than the default plan sizes for
-  moe::WsLayout plan = moe::plan_workspace(T, K, E, P, h->tune.layout_pairs);
-  plan.hist = moe::plan_workspace(T, K, E, P).hist;
+  moe::WsLayout plan = moe::plan_workspace(T, K, E, P, h->tune.layout_pairs, h->pad);
+  plan.hist = sized.hist;
 
   h->has_layout = false;
   h->T = T;
   h->K = K;
   h->E = E;
   h->P = P;
+  h->R = moe::recv_capacity(T, K, E, h->pad);
   h->ws = static_cast<char*>(workspace);
   h->plan = plan;
 
@@ -189,6 +227,8 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
   a.E = E;
   a.P = P;
   a.epr = E / P;
+  a.pad = h->pad;
+  a.R = (int)h->R;
   a.nblk = plan.nblk;
   a.tile = plan.tile;
   a.hist = ws_ptr<int>(h, plan.hist);
@@ -216,8 +256,8 @@ int moe_dispatch(moe_handle_t h, const void* x, int dtype, int64_t H, const floa
   const int st = check_rows(h, dtype, H, &NV);
   if (st != MOE_OK) return st;
   if (scale_rows != 0 && scale_rows != 1) return MOE_ERR_INVALID_ARG;
+  if (h->T == 0) return MOE_OK;  // nothing to read or write; empty arrays may be NULL
   if ((scale_rows || recv_scores) && !topk_weights) return MOE_ERR_INVALID_ARG;
-  if (h->T == 0) return MOE_OK;
   if (!x || !recv) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(recv, 16)) return MOE_ERR_ALIGNMENT;
   if ((topk_weights && !aligned(topk_weights, 4)) || (recv_scores && !aligned(recv_scores, 4)))
@@ -231,11 +271,12 @@ int moe_dispatch(moe_handle_t h, const void* x, int dtype, int64_t H, const floa
   a.T = (int)h->T;
   a.K = h->K;
   a.NV = NV;
-  a.R = (int)(h->T * h->K);
+  a.R = (int)h->R;
   a.dtype = dtype;
   a.scale = scale_rows != 0;
   a.status = ws_ptr<int>(h, h->plan.status);
-  return hip_status(moe::launch_scatter(a, h->tune, stream));
+  const int rc = hip_status(moe::launch_scatter(a, h->tune, stream));
+  return rc != MOE_OK ? rc : fill_padding(h, recv, recv_scores, NV, stream);
 }
 
 int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H, const float* topk_weights,
@@ -255,7 +296,7 @@ int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H, const float
   a.T = (int)h->T;
   a.K = h->K;
   a.NV = NV;
-  a.R = (int)(h->T * h->K);
+  a.R = (int)h->R;
   a.dtype = dtype;
   a.status = ws_ptr<int>(h, h->plan.status);
   return hip_status(moe::launch_gather(a, h->tune, stream));
@@ -267,10 +308,10 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   int NV = 0;
   int st = check_rows(h, dtype, H, &NV);
   if (st != MOE_OK) return st;
-  if (grad_w && (!topk_weights || !y)) return MOE_ERR_INVALID_ARG;
   if (grad_w && (st = check_dot(h, NV)) != MOE_OK) return st;
+  if (h->T == 0) return MOE_OK;  // nothing to read or write; empty arrays may be NULL
+  if (grad_w && (!topk_weights || !y)) return MOE_ERR_INVALID_ARG;
   if (!grad_y && !grad_w) return MOE_ERR_INVALID_ARG;
-  if (h->T == 0) return MOE_OK;
   if (!grad_out) return MOE_ERR_INVALID_ARG;
   if (!aligned(grad_out, 16) || (grad_y && !aligned(grad_y, 16)) || (grad_w && !aligned(y, 16)))
     return MOE_ERR_ALIGNMENT;
@@ -285,11 +326,12 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   a.T = (int)h->T;
   a.K = h->K;
   a.NV = NV;
-  a.R = (int)(h->T * h->K);
+  a.R = (int)h->R;
   a.dtype = dtype;
   a.scale = topk_weights != nullptr;
   a.status = ws_ptr<int>(h, h->plan.status);
   st = grad_y ? hip_status(moe::launch_scatter(a, h->tune, stream)) : MOE_OK;
+  if (st == MOE_OK && grad_y) st = fill_padding(h, grad_y, nullptr, NV, stream);  // no gradient there
   if (st != MOE_OK || !grad_w) return st;
   // router-weight gradient: a separate pass over grad_out and y (measured
   // faster than fusing it into the row stores: HBM turns around less)
@@ -315,10 +357,10 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
   int NV = 0;
   int st = check_rows(h, dtype, H, &NV);
   if (st != MOE_OK) return st;
-  if (grad_s && (!topk_weights || !x)) return MOE_ERR_INVALID_ARG;
   if (grad_s && (st = check_dot(h, NV)) != MOE_OK) return st;
+  if (h->T == 0) return MOE_OK;  // nothing to read or write; empty arrays may be NULL
+  if (grad_s && (!topk_weights || !x)) return MOE_ERR_INVALID_ARG;
   if (!grad_x && !grad_s) return MOE_ERR_INVALID_ARG;
-  if (h->T == 0) return MOE_OK;
   if (!grad_recv) return MOE_ERR_INVALID_ARG;
   if (!aligned(grad_recv, 16) || (grad_x && !aligned(grad_x, 16)) || (grad_s && !aligned(x, 16)))
     return MOE_ERR_ALIGNMENT;
@@ -336,7 +378,7 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
     d.T = (int)h->T;
     d.K = h->K;
     d.NV = NV;
-    d.R = (int)(h->T * h->K);
+    d.R = (int)h->R;
     d.dtype = dtype;
     d.gather = grad_x != nullptr;  // without grad_x: the score gradient only
     d.status = ws_ptr<int>(h, h->plan.status);
@@ -350,10 +392,17 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
   a.T = (int)h->T;
   a.K = h->K;
   a.NV = NV;
-  a.R = (int)(h->T * h->K);
+  a.R = (int)h->R;
   a.dtype = dtype;
   a.status = ws_ptr<int>(h, h->plan.status);
   return hip_status(moe::launch_gather(a, h->tune, stream));
+}
+
+int moe_recv_capacity(moe_handle_t h, int64_t* rows) {
+  if (!valid_handle(h) || !rows) return MOE_ERR_INVALID_ARG;
+  if (!h->has_layout) return MOE_ERR_HANDLE;
+  *rows = h->R;
+  return MOE_OK;
 }
 
 int moe_send_capacity(moe_handle_t h, int64_t* rows) {
@@ -386,7 +435,7 @@ int staged_args(const moe_handle_s* h, int dtype, int64_t H, int64_t send_rows, 
   a->K = h->K;
   a->P = h->P;
   a->NV = NV;
-  a->R = (int)(h->T * h->K);
+  a->R = (int)h->R;
   a->send_cap = (int)cap;
   a->dtype = dtype;
   a->status = ws_ptr<int>(h, h->plan.status);
@@ -417,8 +466,8 @@ int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t s
   const int st = staged_args(h, dtype, H, send_rows, &a);
   if (st != MOE_OK) return st;
   if (scale_rows != 0 && scale_rows != 1) return MOE_ERR_INVALID_ARG;
+  if (h->T == 0) return MOE_OK;  // nothing to read or write; empty arrays may be NULL
   if ((scale_rows || recv_scores) && !topk_weights) return MOE_ERR_INVALID_ARG;
-  if (h->T == 0) return MOE_OK;
   if (!send || !recv) return MOE_ERR_INVALID_ARG;
   if (!aligned(send, 16) || !aligned(recv, 16)) return MOE_ERR_ALIGNMENT;
   if ((topk_weights && !aligned(topk_weights, 4)) || (recv_scores && !aligned(recv_scores, 4)))
@@ -428,7 +477,8 @@ int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t s
   a.w = topk_weights;
   a.scores_out = recv_scores;
   a.scale = scale_rows != 0;
-  return hip_status(moe::launch_expand(a, h->tune, stream));
+  const int rc = hip_status(moe::launch_expand(a, h->tune, stream));
+  return rc != MOE_OK ? rc : fill_padding(h, recv, recv_scores, a.NV, stream);
 }
 
 int moe_reduce_partitions(moe_handle_t h, const void* y, int dtype, int64_t H,
@@ -475,8 +525,8 @@ int moe_handle_field(moe_handle_t h, int field, void** dev_ptr, size_t* bytes) {
     case MOE_FIELD_SEND_OFFSET: off = p.send_offset; n = (P + 1) * 4; break;
     case MOE_FIELD_TOKEN_SLOT: off = p.token_slot; n = T * P * 4; break;
     case MOE_FIELD_RECV_POS: off = p.recv_pos; n = T * K * 4; break;
-    case MOE_FIELD_RECV_TOKEN: off = p.recv_token; n = T * K * 4; break;
-    case MOE_FIELD_RECV_K: off = p.recv_k; n = T * K * 4; break;
+    case MOE_FIELD_RECV_TOKEN: off = p.recv_token; n = (size_t)h->R * 4; break;
+    case MOE_FIELD_RECV_K: off = p.recv_k; n = (size_t)h->R * 4; break;
     case MOE_FIELD_STATUS: off = p.status; n = 4; break;
     case MOE_FIELD_SEND_TOKEN: off = p.send_token; n = T * (K < P ? K : P) * 4; break;
     default: return MOE_ERR_INVALID_ARG;

@@ -19,14 +19,25 @@ struct WsLayout {
   int tile;  // tokens per tile
 };
 
+constexpr int kMaxPadMultiple = 1024;
+
+// Rows of a receive buffer: T*K pairs plus at most pad-1 padding rows per
+// expert segment.
+inline int64_t recv_capacity(int64_t T, int K, int E, int pad) {
+  return T * K + (int64_t)E * (pad - 1);
+}
+
 // layout_pairs: (t,k) pairs per layout tile (512 sizes the workspace: more
-// pairs per tile means fewer tiles and a smaller histogram).
-WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs = kLayoutThreads);
+// pairs per tile means fewer tiles and a smaller histogram).  pad: expert
+// segments padded to a multiple of it (sizes the per-row inverse maps).
+WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs = kLayoutThreads, int pad = 1);
 
 
 struct LayoutArgs {
   const void* idx;
   int itype, T, K, E, P, epr, nblk, tile;
+  int pad;                // expert segments padded to a multiple of this
+  int R;                  // receive rows (recv_capacity)
   int* hist;              // [nblk][E+1+P]: per tile, bucket counts then partition token counts
   unsigned long long* tok_mask;  // [T] partitions each token is sent to
   int* num_tokens_per_expert;
@@ -132,5 +143,18 @@ hipError_t launch_expand(const StagedArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_reduce_partitions(const StagedArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_combine_partitions(const StagedArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// Padding rows of a padded layout: rows [expert_offset[e] + n_e,
+// expert_offset[e+1]) of every expert get zero chunks (and a zero score).
+struct PadArgs {
+  void* dst;                         // [R, NV] chunks
+  float* scores_out;                 // [R] or null
+  const int* expert_offset;          // [E+1], padded
+  const int* num_tokens_per_expert;  // [E]
+  int E, NV, R;
+  int ngrp;                          // wave groups per expert (set by the launcher)
+};
+
+hipError_t launch_pad_fill(const PadArgs& a, const Tuning& t, hipStream_t s);
 
 }  // namespace moe

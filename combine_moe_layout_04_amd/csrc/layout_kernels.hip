@@ -108,13 +108,15 @@ __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
 
 // Start of every histogram column, globally and at tile b.  The histogram is
 // tile-major, h[j * NR + r]: count of column r (a bucket, then a partition)
-// in tile j.  Writes col_0[r] = sum of all columns before r (col_0[NR] = the
-// total) and col_b[r] = col_0[r] + column r's count in the tiles before b.
+// in tile j.  Writes col_n[r] = column r's total, col_0[r] = sum of all
+// columns before r (col_0[NR] = the total) and col_b[r] = col_0[r] + column
+// r's count in the tiles before b.  The first npad columns (the experts)
+// take pad * ceil(total / pad) rows in the running sum: padded segments.
 // Each thread sums a range of tiles of one column with all its loads in
 // flight (clamped, unconditional loads); a workgroup scan over the column
 // totals follows.  part: LDS [2][parts][NR].  Ends with a barrier.
-__device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int b, int* col_b,
-                               int* col_0, int* part, int* wsum) {
+__device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int b, int npad, int pad,
+                               int* col_b, int* col_0, int* col_n, int* part, int* wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
@@ -153,10 +155,11 @@ __device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int 
         pre += part[(parts + q) * NR + r];
       }
     }
-    const int inc = wave_inclusive_scan(tot);
+    const int seg = r < npad ? (tot + pad - 1) / pad * pad : tot;  // rows the column takes
+    const int inc = wave_inclusive_scan(seg);
     if (lane == kWave - 1) wsum[wv] = inc;
     __syncthreads();
-    int st = carry + inc - tot, all = 0;
+    int st = carry + inc - seg, all = 0;
 #pragma unroll
     for (int w = 0; w < kLW; ++w) {
       const int ws = wsum[w];
@@ -166,6 +169,7 @@ __device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int 
     if (r < NR) {
       col_0[r] = st;
       col_b[r] = st + pre;
+      col_n[r] = tot;
     }
     carry += all;
     __syncthreads();  // wsum is rewritten by the next chunk
@@ -186,7 +190,8 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   int* wcnt = wsum + kLW;                    // [kLW][P] per-wave partition counts
   int* wpre = wcnt + kLW * a.P;              // [kLW][P] slots before each wave
   int* carry = wpre + kLW * a.P;             // [P] slots used by earlier token rounds
-  int* part = carry + a.P;                   // [2][parts][NR] scan partials
+  int* coln = carry + a.P;                   // [NR] column totals (unpadded)
+  int* part = coln + NR;                     // [2][parts][NR] scan partials
   uint16_t* ids = reinterpret_cast<uint16_t*>(part + 2 * parts * NR);  // [tile*K]
 
   const int b = blockIdx.x;
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   for (int r = tid; r < a.P; r += kLT) carry[r] = 0;
 
   // 1. global offsets and this tile's starts (the scan ends with a barrier)
-  scan_histogram(a.hist, NR, a.nblk, b, base, off, part, wsum);
+  scan_histogram(a.hist, NR, a.nblk, b, a.E, a.pad, base, off, coln, part, wsum);
 #pragma unroll
   for (int u = 0; u < kIdRegs; ++u) {
     const int i = tid + u * kLT;
@@ -310,7 +315,7 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   }
 
   // 5. stable rank, 64 pairs at a time (all lanes of the wave take part)
-  const int R = a.T * a.K;
+  const int R = a.R;
   const int nbits = 32 - __clz(a.E + 1);  // enough bits for ids 0..E+1
   for (int b0 = w_lo; b0 < w_hi; b0 += kWave) {
     const int i = b0 + lane;
@@ -343,10 +348,27 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
     __builtin_amdgcn_wave_barrier();
   }
 
-  // 6. global counts, offsets and status (tile 0 writes them)
+  // 6. padded layouts: receive rows that hold no pair get -1 in the inverse
+  //    maps; the padding after each expert's pairs (experts strided over the
+  //    tiles), then the rows after the last bucket (split over the tiles)
+  if (a.pad > 1) {  // uniform
+    for (int e = b; e < a.E; e += a.nblk) {
+      const int hi = min(off[e + 1], R);
+      for (int p = off[e] + coln[e] + tid; p < hi; p += kLT) {
+        a.recv_token[p] = -1;
+        a.recv_k[p] = -1;
+      }
+    }
+    for (int p = off[E1] + b * kLT + tid; p < R; p += a.nblk * kLT) {
+      a.recv_token[p] = -1;
+      a.recv_k[p] = -1;
+    }
+  }
+
+  // 7. global counts, offsets and status (tile 0 writes them)
   if (b == 0) {
-    const int total = off[E1];  // T*K: the bucket columns come first
-    for (int e = tid; e < a.E; e += kLT) a.num_tokens_per_expert[e] = off[e + 1] - off[e];
+    const int total = off[E1];  // the bucket columns come first
+    for (int e = tid; e < a.E; e += kLT) a.num_tokens_per_expert[e] = coln[e];
     for (int e = tid; e <= a.E; e += kLT) a.expert_offset[e] = off[e];
     for (int r = tid; r <= a.P; r += kLT) a.rank_offset[r] = off[r * a.epr];
     for (int r = tid; r < a.P; r += kLT) a.num_tokens_per_rank[r] = off[E1 + r + 1] - off[E1 + r];
@@ -364,7 +386,7 @@ size_t layout_count_lds(int E, int P, int tile) {
 size_t layout_rank_lds(int E, int P, int tile, int K) {
   const size_t E1 = (size_t)E + 1, NR = E1 + P;
   const size_t parts_nr = NR > (size_t)kLT ? NR : (size_t)kLT;  // parts * NR <= max(kLT, NR)
-  const size_t ints = NR + (NR + 1) + kLW * E1 + kLW + 2 * (size_t)kLW * P + P + 2 * parts_nr;
+  const size_t ints = NR + (NR + 1) + kLW * E1 + kLW + 2 * (size_t)kLW * P + P + NR + 2 * parts_nr;
   return ints * 4 + (size_t)tile * K * 2;
 }
 

@@ -30,7 +30,9 @@
  *   - Arguments are validated on the host before anything is launched; a
  *     rejected call launches nothing and returns a negative MOE_ERR_* code.
  *   - T = tokens, K = top-k, E = experts, P = partitions (virtual EP ranks),
- *     H = row width in elements, R = T*K receive rows.
+ *     H = row width in elements, R = receive rows: T*K, or T*K + E*(m-1)
+ *     for a handle whose expert segments are padded to a multiple of m
+ *     (moe_handle_create_padded; moe_recv_capacity returns R).
  *   - Expert e belongs to partition e / (E/P); E must be a multiple of P.
  *   - Element types: MOE_F32 (float) or MOE_BF16 (bfloat16 bits).  Every
  *     row is a whole number of 16-byte chunks: H*sizeof(elem) % 16 == 0.
@@ -79,13 +81,14 @@ enum moe_field {
   MOE_FIELD_NUM_TOKENS_PER_EXPERT = 0, /* int32 [E]   (t,k) pairs per expert               */
   MOE_FIELD_NUM_TOKENS_PER_RANK   = 1, /* int32 [P]   distinct tokens per partition         */
   MOE_FIELD_IS_TOKEN_IN_RANK      = 2, /* uint8 [T,P] 1 if any of t's experts is on r       */
-  MOE_FIELD_EXPERT_OFFSET         = 3, /* int32 [E+1] exclusive prefix of expert counts     */
+  MOE_FIELD_EXPERT_OFFSET         = 3, /* int32 [E+1] exclusive prefix of expert segment
+                                          rows (counts, padded to the handle's multiple) */
   MOE_FIELD_RANK_OFFSET           = 4, /* int32 [P+1] first receive row of each partition   */
   MOE_FIELD_SEND_OFFSET           = 5, /* int32 [P+1] exclusive prefix of num_tokens_per_rank */
   MOE_FIELD_TOKEN_SLOT            = 6, /* int32 [T,P] t's slot in r's send list, or -1      */
   MOE_FIELD_RECV_POS              = 7, /* int32 [T,K] receive row of pair (t,k)            */
-  MOE_FIELD_RECV_TOKEN            = 8, /* int32 [R]   token of each receive row            */
-  MOE_FIELD_RECV_K                = 9, /* int32 [R]   k of each receive row                */
+  MOE_FIELD_RECV_TOKEN            = 8, /* int32 [R]   token of each receive row, -1 if none */
+  MOE_FIELD_RECV_K                = 9, /* int32 [R]   k of each receive row, -1 if none     */
   MOE_FIELD_STATUS                = 10,/* int32 [1]   device status bits                   */
   MOE_FIELD_SEND_TOKEN            = 11 /* int32 [T*min(K,P)] token of each send row
                                           (rows >= send_offset[P] unspecified)          */
@@ -106,25 +109,46 @@ typedef struct moe_tuning {
 typedef struct moe_handle_s* moe_handle_t;
 
 /* Bytes of device workspace a layout of this shape needs (pure host).
- * Returns MOE_ERR_* on an invalid shape (same rules as moe_layout). */
+ * Returns MOE_ERR_* on an invalid shape (same rules as moe_layout).  The
+ * _padded form is for handles created with that pad_multiple.  A workspace
+ * sized for the largest T serves every smaller T: calls with a varying
+ * number of tokens need no new allocation. */
 int moe_workspace_size(int64_t T, int K, int E, int P, size_t* bytes);
+int moe_workspace_size_padded(int64_t T, int K, int E, int P, int pad_multiple, size_t* bytes);
 
 /* Create / destroy a handle.  `tuning` may be NULL.  Host memory only: the
  * handle records views into the caller's workspace, never owns device memory. */
 int moe_handle_create(moe_handle_t* out, const moe_tuning* tuning);
 int moe_handle_destroy(moe_handle_t h);
 
+/* A handle whose layouts pad every expert's segment of receive rows to a
+ * multiple of pad_multiple (1..1024; 1 = moe_handle_create), fixed for the
+ * handle's life (the DiffusionGemma dispatcher page lists pad_multiple as
+ * set once at construction).  Segment e holds its n_e pairs, in the usual
+ * order, then pad_multiple*ceil(n_e/pad_multiple) - n_e padding rows, so
+ * every expert_offset is a multiple of pad_multiple (grouped-GEMM tiles).
+ * Calls that write receive rows (moe_dispatch, moe_expand, the grad_y rows
+ * of moe_combine_bwd) write zero rows there, and zero scores when they write
+ * scores (the zero-sentinel scores of the padded permute, "[MoE] Apply
+ * router scores before W2 projection", "Implementation"); rows past
+ * expert_offset[E] are not written.  Calls that read receive rows never
+ * read padding.  Receive buffers hold R = T*K + E*(pad_multiple-1) rows. */
+int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pad_multiple);
+
 /* Layout of one routing decision (method steps: counts, offsets, stable
  * positions).  Fills every handle field inside `workspace`.
  *
  *   topk_idx   [T,K] int32 (itype MOE_I32) or int64 (MOE_I64), device.
- *   workspace  device, >= moe_workspace_size(T,K,E,P) bytes, 256-byte aligned;
- *              it holds the handle's arrays and must outlive every later call
- *              on this handle.
+ *   workspace  device, >= moe_workspace_size(T,K,E,P) bytes (the _padded
+ *              size for a padded handle), 256-byte aligned; it holds the
+ *              handle's arrays and must outlive every later call on this
+ *              handle.  MOE_ERR_WORKSPACE if it is smaller.
  *
  * Definitions (oracle: stable counting sort of the (t,k) pairs by expert):
  *   recv_pos[t,k] = expert_offset[e] + #{(t',k') < (t,k) lexicographically
  *                    with topk_idx[t',k'] == e},  e = topk_idx[t,k];
+ *   expert_offset[e] = sum over e' < e of n_e' (rounded up to the handle's
+ *                    pad multiple, see moe_handle_create_padded);
  *   so rows are grouped by expert in ascending id (hence by partition), and
  *   inside an expert by token, then k.  The order depends on the routing
  *   only, so an activation-checkpoint replay of the same routing reproduces
@@ -135,7 +159,9 @@ int moe_handle_destroy(moe_handle_t h);
  *   increasing t (a token is sent once per partition, not once per expert:
  *   the deduplication of the DeepSpeed transport PR's "Why" section).
  *
- * T = 0 is valid and yields an empty layout.  Entries of topk_idx outside
+ * T = 0 is valid and yields an empty layout; every data call on it returns
+ * MOE_OK after its non-pointer checks, reads and writes nothing, and accepts
+ * NULL for any array (an empty tensor's data pointer).  Entries of topk_idx outside
  * [0,E) are an input error detected on the device: MOE_STATUS_BAD_EXPERT is
  * set and those pairs are placed after the last expert's rows (so every
  * position stays inside [0,R)); the other fields are then unspecified.
@@ -222,6 +248,11 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
 /* Rows a send buffer must hold: T * min(K, P), an upper bound of send_offset[P]. */
 int moe_send_capacity(moe_handle_t h, int64_t* rows);
 
+/* Rows a receive buffer (recv, y, grad_y, grad_recv, recv_scores) holds for
+ * the current layout: T*K, plus E*(pad_multiple-1) on a padded handle.
+ * Known on the host; no device sync. */
+int moe_recv_capacity(moe_handle_t h, int64_t* rows);
+
 /* Source side: send[send_offset[r] + token_slot[t,r]] = x[t] for every
  * partition r of token t (each x row is read once).  x [T,H].            */
 int moe_send(moe_handle_t h, const void* x, int dtype, int64_t H, void* send, int64_t send_rows,
@@ -229,7 +260,8 @@ int moe_send(moe_handle_t h, const void* x, int dtype, int64_t H, void* send, in
 
 /* Receiver side: recv[recv_pos[t,k]] = send[send_offset[r] + token_slot[t,r]]
  * for every pair whose expert is on partition r (each send row is read
- * once); scale_rows and recv_scores as in moe_dispatch.  recv [T*K,H].    */
+ * once); scale_rows, recv_scores and padding rows as in moe_dispatch.
+ * recv [R,H].                                                             */
 int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t send_rows,
                const float* topk_weights, int scale_rows, void* recv, float* recv_scores,
                hipStream_t stream);
@@ -238,7 +270,7 @@ int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t s
  * row, partial = round(sum [w[t,k] *] y[recv_pos[t,k]]) over the token's k
  * with an expert on that partition, in k order, float32 from +0.0 (product
  * and sum rounded on their own); rounded to the row type, the type a
- * transport sends.  y [T*K,H]; partial [send_rows,H]; weights may be NULL
+ * transport sends.  y [R,H]; partial [send_rows,H]; weights may be NULL
  * (plain sum).                                                             */
 int moe_reduce_partitions(moe_handle_t h, const void* y, int dtype, int64_t H,
                           const float* topk_weights, void* partial, int64_t send_rows,

@@ -147,3 +147,35 @@ def test_strerror_and_version(L):
     for name, code in C.items():
         assert L.moe_strerror(code)
     assert b"gfx950" in L.moe_version()
+
+
+def test_padded_handle_and_workspace_rules(L):
+    h = ctypes.c_void_p()
+    for bad in (0, -1, 1025):
+        assert L.moe_handle_create_padded(ctypes.byref(h), None, bad) == C["MOE_ERR_INVALID_ARG"]
+    n1, n = ctypes.c_size_t(), ctypes.c_size_t()
+    T, K, E, P = 4096, 8, 128, 8
+    assert L.moe_workspace_size(T, K, E, P, ctypes.byref(n1)) == 0
+    assert L.moe_workspace_size_padded(T, K, E, P, 1, ctypes.byref(n)) == 0 and n.value == n1.value
+    for m in (2, 16, 128, 1024):
+        assert L.moe_workspace_size_padded(T, K, E, P, m, ctypes.byref(n)) == 0
+        extra = 2 * E * (m - 1) * 4          # the two per-row inverse maps grow with the padding
+        assert extra <= n.value - n1.value <= extra + 512
+    assert L.moe_workspace_size_padded(T, K, E, P, 0, ctypes.byref(n)) == C["MOE_ERR_INVALID_ARG"]
+    # capacity T*K + E*(m-1) must stay below 2^31
+    T2 = ((1 << 31) - 8) // 8
+    assert L.moe_workspace_size_padded(T2, 8, 128, 8, 1, ctypes.byref(n)) == 0
+    assert L.moe_workspace_size_padded(T2, 8, 128, 8, 1024, ctypes.byref(n)) == C["MOE_ERR_UNSUPPORTED"]
+    assert L.moe_handle_create_padded(ctypes.byref(h), None, 64) == 0
+    try:
+        rows = ctypes.c_int64()
+        assert L.moe_recv_capacity(h, ctypes.byref(rows)) == C["MOE_ERR_HANDLE"]
+        assert L.moe_recv_capacity(None, ctypes.byref(rows)) == C["MOE_ERR_INVALID_ARG"]
+        L.moe_workspace_size_padded(64, 8, 128, 8, 64, ctypes.byref(n))
+        L.moe_workspace_size(64, 8, 128, 8, ctypes.byref(n1))
+        ws, idx = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE)
+        # an unpadded size is too small for a padded handle: rejected before any launch
+        assert L.moe_layout(h, idx, 0, 64, 8, 128, 8, ws, n1.value, None) == C["MOE_ERR_WORKSPACE"]
+        assert L.moe_layout(h, idx, 0, 64, 8, 128, 8, ws, n.value - 1, None) == C["MOE_ERR_WORKSPACE"]
+    finally:
+        L.moe_handle_destroy(h)
