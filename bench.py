@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--staged", action="store_true",
                     help="staged exchange: send buffer per destination partition, receiver-side "
                          "expansion, two-level combine")
+    ap.add_argument("--pad-multiple", type=int, default=1,
+                    help="pad every expert's receive segment to a multiple of this (zero rows)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph (no per-call events)")
     return ap.parse_args()
@@ -70,34 +72,46 @@ def parse():
 # The step: a list of calls, each with its algorithmic row bytes
 # --------------------------------------------------------------------------
 
-def step_calls(cfg, staged=False, n_send=None):
+# calls that write receive rows: with a padded layout they also write the
+# zero padding rows of every expert segment
+PADDING_WRITERS = ("dispatch", "dispatch_scaled", "combine_bwd", "combine_bwd_plain",
+                   "expand_x", "expand_x_scaled", "expand_g", "expand_g_w")
+
+
+def step_calls(cfg, staged=False, n_send=None, pad_rows=None):
     """[(name, kind, pass, algorithmic row bytes)] of one step, in order.
 
     Row bytes only (index and weight traffic, about 4-12 bytes per (t,k)
     pair per call, are reported apart): TH = T*H*b token-row bytes, RH =
     T*K*H*b receive-row bytes, NS = N_send*H*b send-buffer bytes (one row
-    per (token, destination partition) pair; n_send[p] for pass p).
+    per (token, destination partition) pair; n_send[p] for pass p).  With a
+    padded layout, pad_rows[p] zero rows are added to each write of
+    receive rows.
     """
     TH = cfg.T * cfg.H * cfg.esize
     RH = cfg.R * cfg.H * cfg.esize
     if staged:
-        return _staged_calls(cfg, TH, RH, [n * cfg.H * cfg.esize for n in n_send])
-    if not cfg.absorbed:
-        return [("layout", "layout", 0, 0),
-                ("dispatch", "dispatch", 0, TH + RH),
-                ("combine", "combine", 0, RH + TH),
-                ("combine_bwd", "combine_bwd", 0, TH + 2 * RH),
-                ("dispatch_bwd", "dispatch_bwd", 0, RH + TH)]
-    calls = []
-    for p in range(3):
-        calls += [(f"layout.{p}", "layout", p, 0),
-                  (f"dispatch.{p}", "dispatch_scaled", p, TH + RH),
-                  (f"combine.{p}", "combine_plain", p, RH + TH)]
-    for p in (0, 2):
-        calls += [(f"replay_layout.{p}", "layout", p, 0),
-                  (f"replay_dispatch.{p}", "dispatch_scaled", p, TH + RH),
-                  (f"combine_bwd.{p}", "combine_bwd_plain", p, TH + RH),
-                  (f"dispatch_bwd.{p}", "dispatch_bwd_scaled", p, RH + 2 * TH)]
+        calls = _staged_calls(cfg, TH, RH, [n * cfg.H * cfg.esize for n in n_send])
+    elif not cfg.absorbed:
+        calls = [("layout", "layout", 0, 0),
+                 ("dispatch", "dispatch", 0, TH + RH),
+                 ("combine", "combine", 0, RH + TH),
+                 ("combine_bwd", "combine_bwd", 0, TH + 2 * RH),
+                 ("dispatch_bwd", "dispatch_bwd", 0, RH + TH)]
+    else:
+        calls = []
+        for p in range(3):
+            calls += [(f"layout.{p}", "layout", p, 0),
+                      (f"dispatch.{p}", "dispatch_scaled", p, TH + RH),
+                      (f"combine.{p}", "combine_plain", p, RH + TH)]
+        for p in (0, 2):
+            calls += [(f"replay_layout.{p}", "layout", p, 0),
+                      (f"replay_dispatch.{p}", "dispatch_scaled", p, TH + RH),
+                      (f"combine_bwd.{p}", "combine_bwd_plain", p, TH + RH),
+                      (f"dispatch_bwd.{p}", "dispatch_bwd_scaled", p, RH + 2 * TH)]
+    if pad_rows:
+        calls = [(n, k, p, b + (pad_rows[p] * cfg.H * cfg.esize if k in PADDING_WRITERS else 0))
+                 for n, k, p, b in calls]
     return calls
 
 
@@ -138,7 +152,7 @@ def _staged_calls(cfg, TH, RH, NS):
     return calls
 
 
-def index_bytes(cfg, staged=False, n_send=None):
+def index_bytes(cfg, staged=False, n_send=None, pad_rows=None):
     """Index, weight and score traffic per step (reported apart from `value`)."""
     R, T = cfg.R, cfg.T
     per = {"layout": R * 4 * 2 + R * 4 * 3 + T * cfg.P * 5 + T * 8 * 2 + T * 8,
@@ -153,7 +167,7 @@ def index_bytes(cfg, staged=False, n_send=None):
     for kind, words in (("expand_x", 3), ("expand_x_scaled", 3), ("expand_g", 1), ("expand_g_w", 2),
                         ("reduce_y_w", 2), ("reduce_y", 1), ("reduce_gr", 1), ("reduce_gr_w", 2)):
         per[kind] = R * 4 * words + ns
-    return sum(per[kind] for _, kind, _, _ in step_calls(cfg, staged, n_send))
+    return sum(per[kind] for _, kind, _, _ in step_calls(cfg, staged, n_send, pad_rows))
 
 
 # The call whose kernel the roofline reports: the K-row gather-reduce (in the
@@ -242,17 +256,25 @@ class HipEvents:
 # CPU baseline: the oracle, untuned, on a bounded sample of the same step
 # --------------------------------------------------------------------------
 
-def cpu_baseline(cfg, budget_s, staged=False):
+def cpu_baseline(cfg, budget_s, staged=False, pad_multiple=1):
     import numpy as np
 
     import workloads as W
     from oracle import moe_oracle as O
 
     dt = cfg.dtype
+    m = pad_multiple
     passes = 3 if cfg.absorbed else 1
     inps = [W.layer_inputs(cfg, seed=0, pss=p) for p in range(passes)]
-    lays = [O.layout(inp.topk_idx, cfg.E, cfg.P) for inp in inps]
-    calls = step_calls(cfg, staged, [l.n_send for l in lays])
+    if m > 1:  # receive-row inputs span the padded capacity
+        extra = cfg.E * (m - 1)
+        inps = [i.__class__(i.cfg, i.topk_idx, i.topk_weights, i.x,
+                            np.concatenate([i.y, np.zeros((extra, cfg.H), i.y.dtype)]), i.g,
+                            np.concatenate([i.grad_recv, np.zeros((extra, cfg.H), i.y.dtype)]))
+                for i in inps]
+    lays = [O.layout(inp.topk_idx, cfg.E, cfg.P, m) for inp in inps]
+    calls = step_calls(cfg, staged, [l.n_send for l in lays],
+                       [int(l.expert_offset[-1]) - cfg.R for l in lays])
     step_b = sum(b for _, _, _, b in calls)
     lay = {}
     st = {}  # staged: the last send buffer and partial rows of each pass
@@ -265,7 +287,7 @@ def cpu_baseline(cfg, budget_s, staged=False):
             inp = inps[p]
             w = inp.topk_weights
             if kind == "layout":
-                lay[p] = L = O.layout(inp.topk_idx, cfg.E, cfg.P)
+                lay[p] = L = O.layout(inp.topk_idx, cfg.E, cfg.P, m)
             L = lay[p]
             if kind == "dispatch":
                 O.dispatch(L, inp.x, dt, w)
@@ -352,6 +374,11 @@ def main():
     # gradients are shared by the passes
     base = W.layer_inputs(cfg, seed=0)
     y0, g0, gr0 = (dev_rows(a) for a in (base.y, base.g, base.grad_recv))
+    m = args.pad_multiple
+    RC = cfg.R + cfg.E * (m - 1)  # receive rows: T*K plus the padding capacity
+    if RC > cfg.R:
+        y0, gr0 = (torch.cat([a, torch.zeros((RC - cfg.R, cfg.H), dtype=a.dtype, device=dev)])
+                   for a in (y0, gr0))
     per_pass = []
     for p in range(passes):
         inp = base if p == 0 else W.layer_inputs(cfg, seed=0, pss=p, with_rows=False)
@@ -363,7 +390,7 @@ def main():
         return torch.empty((n, cfg.H), dtype=tdt, device=dev)
 
     nsets = 1 if args.warm else max(1, args.sets)
-    ws_bytes = M.moe_workspace_size(cfg.T, cfg.K, cfg.E, cfg.P)
+    ws_bytes = M.moe_workspace_size(cfg.T, cfg.K, cfg.E, cfg.P, m)
     sets = []
     for _ in range(nsets):
         s = {"pass": [], "y": y0.clone(), "g": g0.clone()}
@@ -373,15 +400,22 @@ def main():
         for idx, w, x in per_pass:
             s["pass"].append(dict(
                 idx=idx.clone(), w=w.clone(), x=x.clone(),
-                recv=empty_rows(cfg.R), scores=torch.empty(cfg.R, dtype=torch.float32, device=dev),
+                recv=empty_rows(RC), scores=torch.empty(RC, dtype=torch.float32, device=dev),
                 out=empty_rows(cfg.T),
                 ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
-                h=M.Handle(args.chunks_per_lane, args.nontemporal, args.waves_per_block, args.layout_pairs)))
-        s["grad_y"] = empty_rows(cfg.R)
+                h=M.Handle(args.chunks_per_lane, args.nontemporal, args.waves_per_block, args.layout_pairs,
+                           pad_multiple=m)))
+        s["grad_y"] = empty_rows(RC)
         s["grad_w"] = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device=dev)
         s["grad_x"] = empty_rows(cfg.T)
         sets.append(s)
     del y0, g0, gr0, per_pass
+
+    # padding rows of each pass's routing (the same in every buffer set)
+    pad_rows = []
+    for q in sets[0]["pass"]:
+        M.moe_layout(q["idx"], cfg.E, cfg.P, handle=q["h"], workspace=q["ws"])
+        pad_rows.append(int(q["h"].field("expert_offset")[-1].item()) - cfg.R)
 
     n_send = None
     if args.staged:
@@ -406,7 +440,7 @@ def main():
                     n_send.append(int(q["h"].field("send_offset")[-1].item()))
     torch.cuda.synchronize()
 
-    calls = step_calls(cfg, args.staged, n_send)
+    calls = step_calls(cfg, args.staged, n_send, pad_rows)
     names = [c[0] for c in calls]
     ncall = len(calls)
     dom = dominant_call(cfg, args.staged)
@@ -546,6 +580,8 @@ def main():
     if args.staged:
         protocol += ("; staged exchange: dispatch = send + expand, combine = reduce_partitions + "
                      "combine_partitions, router-side gradients as row-free dot calls")
+    if m > 1:
+        protocol += f"; expert segments padded to a multiple of {m} (zero rows and scores)"
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -568,7 +604,8 @@ def main():
             "call_avg_us": {n: round(v, 2) for n, v in avg_us.items()},
             "call_median_us": {n: round(v, 2) for n, v in med_us.items()},
             "call_GBps": {n: round(row_bytes[n] / (avg_us[n] * 1e-6) / 1e9, 1) for n in avg_us if row_bytes[n]},
-            "index_bytes_per_step": index_bytes(cfg, args.staged, n_send),
+            "index_bytes_per_step": index_bytes(cfg, args.staged, n_send, pad_rows),
+            **({} if m == 1 else {"pad_multiple": m, "padding_rows": pad_rows}),
             "host_enqueue_us_per_step": round(host_us, 1),
             "timing": ("hip graph replay" if graphs is not None else "eager launches") +
                       f", events: {args.events if graphs is None else 'none'}",
@@ -599,7 +636,7 @@ def main():
             "algorithmic_bytes_per_launch": row_bytes[dom],
             "avg_launch_us": round(dom_us, 2),
         },
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds, args.staged),
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds, args.staged, m),
     }
     print(json.dumps(line), flush=True)
 

@@ -109,6 +109,7 @@ int check_rows(const moe_handle_s* h, int dtype, int64_t H, int* NV) {
   if (nv >= (int64_t(1) << 31) || nv * h->R >= (int64_t(1) << 62)) return MOE_ERR_UNSUPPORTED;
   // one wave per (token, segment): the grid must fit in a 32-bit wave index
   if (moe::row_waves(h->T, (int)nv, 1) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (h->pad > 1 && moe::pad_fill_waves(h->E, h->pad, (int)nv) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   *NV = (int)nv;
   return MOE_OK;
 }
@@ -137,6 +138,7 @@ int fill_padding(const moe_handle_s* h, void* rows, float* scores, int NV, hipSt
   p.E = h->E;
   p.NV = NV;
   p.R = (int)h->R;
+  p.pad = h->pad;
   return hip_status(moe::launch_pad_fill(p, h->tune, stream));
 }
 

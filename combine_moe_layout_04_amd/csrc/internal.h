@@ -152,9 +152,13 @@ struct PadArgs {
   const int* expert_offset;          // [E+1], padded
   const int* num_tokens_per_expert;  // [E]
   int E, NV, R;
-  int ngrp;                          // wave groups per expert (set by the launcher)
+  int pad;                           // the handle's multiple: at most pad-1 padding rows per expert
+  int ngrp;                          // segments per row (set by the launcher)
+  int nblk;                          // row blocks per expert (set by the launcher)
 };
 
+// Wavefronts of one padding fill (its wave index must fit in 32 bits).
+int64_t pad_fill_waves(int E, int pad, int NV);
 hipError_t launch_pad_fill(const PadArgs& a, const Tuning& t, hipStream_t s);
 
 }  // namespace moe
