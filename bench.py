@@ -63,6 +63,11 @@ def parse():
                          "expansion, two-level combine")
     ap.add_argument("--pad-multiple", type=int, default=1,
                     help="pad every expert's receive segment to a multiple of this (zero rows)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="the step beside a stand-in expert GEMM: alone, concurrent on two streams, and "
+                         "with the step on a CU-masked stream of each --budgets size")
+    ap.add_argument("--budgets", default="32,64,96,128,160,192",
+                    help="CU budgets of the exchange for --overlap")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph (no per-call events)")
     return ap.parse_args()
@@ -340,6 +345,108 @@ def cpu_baseline(cfg, budget_s, staged=False, pad_multiple=1):
 
 
 # --------------------------------------------------------------------------
+# Overlap with a stand-in expert GEMM, and the exchange's CU budget
+# --------------------------------------------------------------------------
+
+# Qwen3-30B-A3B's expert FFN width: the stand-in GEMM is the layer's gate+up
+# projection, [T*K, H] x [H, 2*768], in bf16.
+EXPERT_FFN = 768
+
+
+def overlap_run(args, cfg, step, sets, nsets, calls, n_send, pad_rows):
+    """Exchange steps and stand-in GEMMs, K of each: alone on the full GPU,
+    concurrent on two ordinary streams, and for every CU budget N concurrent
+    with the exchange on CUs [0, N) and the GEMM on the other CUs (each
+    also timed alone on its CUs).  Wall time for all K of both."""
+    import torch
+
+    import combine_moe_layout_04_amd as M
+
+    dev = torch.device("cuda:0")
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    R, H, F2 = cfg.R, cfg.H, 2 * EXPERT_FFN
+    A = [torch.randn((R, H), device=dev).to(torch.bfloat16) for _ in range(2)]
+    B = torch.randn((H, F2), device=dev).to(torch.bfloat16).contiguous()
+    C = [torch.empty((R, F2), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    K = args.steps
+    gemm_flop = 2.0 * R * H * F2
+
+    def gemm(i):
+        torch.matmul(A[i % 2], B, out=C[i % 2])
+
+    def xstep(i):
+        step(sets[i % nsets])
+
+    def timed(parts):
+        """parts: [(stream or None, fn(i))], enqueued interleaved so that both
+        streams stay fed; wall us per iteration (K of each)."""
+        cur = torch.cuda.current_stream()
+
+        def run(n):
+            for i in range(n):
+                for st, fn in parts:
+                    with torch.cuda.stream(st if st is not None else cur):
+                        fn(i)
+
+        run(max(2, args.warmup // 4))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(K)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / K
+
+    t_x = timed([(None, xstep)])
+    t_g = timed([(None, gemm)])
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    t_both = timed([(sa, xstep), (sb, gemm)])
+    rows = []
+    for n in [int(b) for b in args.budgets.split(",") if b]:
+        if not 0 < n < ncu:
+            continue
+        xs, gs = M.CuBudgetStream(0, n), M.CuBudgetStream(n, ncu - n)
+        try:
+            tx = timed([(xs.stream, xstep)])
+            tg = timed([(gs.stream, gemm)])
+            tb = timed([(xs.stream, xstep), (gs.stream, gemm)])
+            # only the exchange confined: the GEMM may use every CU
+            tbf = timed([(xs.stream, xstep), (sb, gemm)])
+        finally:
+            xs.close()
+            gs.close()
+        rows.append({"exchange_cus": n, "gemm_cus": ncu - n, "exchange_alone_us": round(tx, 2),
+                     "gemm_alone_us": round(tg, 2), "concurrent_us": round(tb, 2),
+                     "speedup_vs_serial": round((t_x + t_g) / tb, 3),
+                     "concurrent_gemm_unmasked_us": round(tbf, 2),
+                     "speedup_gemm_unmasked": round((t_x + t_g) / tbf, 3)})
+    best = min(rows, key=lambda r: min(r["concurrent_us"], r["concurrent_gemm_unmasked_us"])) if rows else None
+    step_b = sum(b for *_, b in calls)
+    line = {
+        "metric": "exchange step beside a stand-in expert GEMM: wall us per (step + GEMM)",
+        "value": round(min(best["concurrent_us"], best["concurrent_gemm_unmasked_us"]) if best else t_both, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "higher_is_better": False,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: T={cfg.T} H={H} {cfg.dtype} E={cfg.E} P={cfg.P} K={cfg.K}; "
+                        f"stand-in GEMM [{R},{H}]x[{H},{F2}] bf16 (gate+up projection of the experts)",
+            "exchange_alone_us": round(t_x, 2),
+            "exchange_TBps": round(step_b / (t_x * 1e-6) / 1e12, 3),
+            "gemm_alone_us": round(t_g, 2),
+            "gemm_TFLOPs": round(gemm_flop / (t_g * 1e-6) / 1e12, 1),
+            "serial_us": round(t_x + t_g, 2),
+            "concurrent_two_streams_us": round(t_both, 2),
+            "speedup_two_streams": round((t_x + t_g) / t_both, 3),
+            "cu_budgets": rows,
+            "best_budget_cus": best["exchange_cus"] if best else None,
+            "cus": ncu,
+        },
+    }
+    print(json.dumps(line), flush=True)
+
 
 def main():
     args = parse()
@@ -510,6 +617,10 @@ def main():
     for s in sets:
         for q in s["pass"]:
             assert q["h"].check() == 0
+
+    if args.overlap:
+        overlap_run(args, cfg, step, sets, nsets, calls, n_send, pad_rows)
+        return
 
     graphs = None
     if args.graph:

@@ -5,6 +5,7 @@ The hot path is hand-written HIP in ``csrc/`` behind the C ABI of
 """
 from .api import (  # noqa: F401
     FIELDS,
+    CuBudgetStream,
     Handle,
     MoeError,
     moe_bench_copy,

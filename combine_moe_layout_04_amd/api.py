@@ -377,6 +377,33 @@ def moe_combine_partitions(handle: Handle, partial: torch.Tensor,
     return out
 
 
+class CuBudgetStream:
+    """A HIP stream restricted to compute units [cu_first, cu_first + cu_count)
+    (moe_stream_create_cu_budget), usable as a torch stream (`.stream`)."""
+
+    def __init__(self, cu_first: int, cu_count: int, device=None):
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        with torch.cuda.device(dev):
+            s = ctypes.c_void_p()
+            _check(lib().moe_stream_create_cu_budget(int(cu_first), int(cu_count), ctypes.byref(s)),
+                   "moe_stream_create_cu_budget")
+        self._s = s
+        self.cu_first, self.cu_count = int(cu_first), int(cu_count)
+        self.stream = torch.cuda.ExternalStream(s.value, device=dev)
+
+    def close(self):
+        if getattr(self, "_s", None) is not None and self._s.value:
+            self.stream.synchronize()
+            lib().moe_stream_destroy(self._s)
+            self._s = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def moe_bench_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     """Plain device copy (calibration kernel for HBM traffic counters)."""
     if dst.numel() * dst.element_size() != src.numel() * src.element_size():

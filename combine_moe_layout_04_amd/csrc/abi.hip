@@ -566,6 +566,30 @@ int moe_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream)
   return hip_status(moe::launch_copy(dst, src, bytes, stream));
 }
 
+int moe_stream_create_cu_budget(int cu_first, int cu_count, hipStream_t* out) {
+  if (!out || cu_first < 0 || cu_count < 1) return MOE_ERR_INVALID_ARG;
+  int dev = 0, ncu = 0, nxcc = 1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (hipDeviceGetAttribute(&nxcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess) nxcc = 1;
+  // every selected CU must exist (an empty mask would leave the stream's work
+  // with no CU to run on), and the runtime numbers CUs round-robin over the
+  // XCDs and refuses a mask that leaves one without a CU: a budget takes at
+  // least one CU per XCD
+  if (ncu < 1 || cu_first + (int64_t)cu_count > ncu || cu_count < nxcc) return MOE_ERR_SHAPE;
+  uint32_t mask[64] = {};  // up to 2048 CUs
+  const int words = (ncu + 31) / 32;
+  if (words > 64) return MOE_ERR_UNSUPPORTED;
+  for (int c = cu_first; c < cu_first + cu_count; ++c) mask[c / 32] |= 1u << (c % 32);
+  return hip_status(hipExtStreamCreateWithCUMask(out, (uint32_t)words, mask));
+}
+
+int moe_stream_destroy(hipStream_t stream) {
+  if (!stream) return MOE_ERR_INVALID_ARG;
+  return hip_status(hipStreamDestroy(stream));
+}
+
 const char* moe_strerror(int status) {
   switch (status) {
     case MOE_OK: return "ok";

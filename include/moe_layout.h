@@ -290,6 +290,25 @@ int moe_handle_dims(moe_handle_t h, int64_t* T, int* K, int* E, int* P);
 /* Synchronises `stream`, then reads the device status word (MOE_STATUS_* bits). */
 int moe_handle_check(moe_handle_t h, hipStream_t stream, int* device_status);
 
+/* ---- CU budget -------------------------------------------------------------
+ * A stream whose kernels may run only on compute units [cu_first, cu_first +
+ * cu_count) of the current device (a hardware CU mask; default priority).
+ * The exchange calls issued on it use at most that many CUs, and a GEMM on a
+ * stream with the other CUs runs beside them: the analogue of the SM budget
+ * of the pages' transport kernels ("Add an opt-in DeepEP transport for the
+ * AutoEP expert all-to-all", section "Choosing the SM budget": the exchange
+ * competes with the expert GEMM for SMs, so the budget was chosen on whole
+ * steps; its follow-up list names communication/compute overlap).  CU
+ * indices are the HIP runtime's, numbered round-robin over the XCDs, so a
+ * range of consecutive indices spreads evenly over them; the runtime refuses
+ * a mask that leaves an XCD without a CU, so cu_count is at least the XCD
+ * count (8 on MI355X).  MOE_ERR_INVALID_ARG for a NULL out, cu_first < 0 or
+ * cu_count < 1; MOE_ERR_SHAPE if the range passes the device's CU count or
+ * holds fewer CUs than XCDs; MOE_ERR_HIP if the runtime refuses.  Destroy
+ * with moe_stream_destroy.                                                 */
+int moe_stream_create_cu_budget(int cu_first, int cu_count, hipStream_t* out);
+int moe_stream_destroy(hipStream_t stream);
+
 /* Plain device copy of `bytes` (multiple of 16, 16-byte aligned pointers):
  * the reference kernel for calibrating HBM traffic counters against a known
  * byte count.  Not part of the method.                                    */

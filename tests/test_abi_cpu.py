@@ -179,3 +179,11 @@ def test_padded_handle_and_workspace_rules(L):
         assert L.moe_layout(h, idx, 0, 64, 8, 128, 8, ws, n.value - 1, None) == C["MOE_ERR_WORKSPACE"]
     finally:
         L.moe_handle_destroy(h)
+
+
+def test_cu_budget_stream_validation(L):
+    s = ctypes.c_void_p()
+    assert L.moe_stream_create_cu_budget(0, 8, None) == C["MOE_ERR_INVALID_ARG"]
+    assert L.moe_stream_create_cu_budget(-1, 8, ctypes.byref(s)) == C["MOE_ERR_INVALID_ARG"]
+    assert L.moe_stream_create_cu_budget(0, 0, ctypes.byref(s)) == C["MOE_ERR_INVALID_ARG"]
+    assert L.moe_stream_destroy(None) == C["MOE_ERR_INVALID_ARG"]
