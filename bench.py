@@ -68,6 +68,8 @@ def parse():
                          "with the step on a CU-masked stream of each --budgets size")
     ap.add_argument("--budgets", default="32,64,96,128,160,192",
                     help="CU budgets of the exchange for --overlap")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the 1 GiB copy that measures the achievable HBM ceiling")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph (no per-call events)")
     return ap.parse_args()
@@ -337,6 +339,8 @@ def cpu_baseline(cfg, budget_s, staged=False, pad_multiple=1):
         "value": round(moved / el / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
+        "host_cpus": os.cpu_count(),
+        "cpu_affinity": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{done_steps} whole steps + {n_calls - done_steps * len(calls)} calls of the "
                   f"{cfg.name} {'staged ' if staged else ''}step (T={cfg.T}, H={cfg.H}, {dt}; "
@@ -649,13 +653,19 @@ def main():
     per_step = 2 * len(timed)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     hev = HipEvents(per_step * K)
+    step_events = args.events != "none"
+    sev = HipEvents(K + 1 if step_events else 0)  # step boundaries
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        if step_events:
+            sev.record(i, stream)
         if graphs is not None:
             graphs[i % nsets].replay()
         else:
             step(sets[i % nsets], per_step * i)
+    if step_events:
+        sev.record(K, stream)
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -668,6 +678,41 @@ def main():
     hev.close()
     avg_us = {n: float(np.mean(v)) * 1e3 for n, v in call_ms.items()}
     med_us = {n: float(np.median(v)) * 1e3 for n, v in call_ms.items()}
+    step_us = None
+    if step_events:
+        st = np.array([sev.elapsed_ms(i, i + 1) for i in range(K)]) * 1e3
+        step_us = {"median": round(float(np.median(st)), 2), "p10": round(float(np.percentile(st, 10)), 2),
+                   "p90": round(float(np.percentile(st, 90)), 2)}
+    sev.close()
+    per_pass = None
+    if cfg.absorbed and len(avg_us) == ncall:
+        # each forward pass, and each replay + backward
+        def of_pass(n, p):
+            return n.endswith(f".{p}") or f".{p}:" in n
+
+        per_pass = {f"fwd.{p}": round(sum(v for n, v in avg_us.items()
+                                          if n.startswith(("layout.", "dispatch.", "combine.")) and of_pass(n, p)), 2)
+                    for p in range(3)}
+        per_pass.update({f"replay_bwd.{p}": round(sum(v for n, v in avg_us.items()
+                                                      if n.startswith(("replay_", "combine_bwd", "dispatch_bwd"))
+                                                      and of_pass(n, p)), 2)
+                         for p in (0, 2)})
+
+    # the achievable ceiling: a plain device copy of 1 GiB (2 GiB moved), median of 5
+    ceiling = None
+    if not args.no_ceiling:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        cev = HipEvents(12)
+        for i in range(6):
+            cev.record(2 * i, stream)
+            M.moe_bench_copy(dst, src)
+            cev.record(2 * i + 1, stream)
+        torch.cuda.synchronize()
+        cus = sorted(cev.elapsed_ms(2 * i, 2 * i + 1) * 1e3 for i in range(1, 6))
+        cev.close()
+        del src, dst
+        ceiling = round(2.0 * (1 << 30) / (cus[2] * 1e-6) / 1e9, 1)
 
     # the copy kernel of known size, untimed: calibrates the traffic counters
     cbuf = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
@@ -718,6 +763,8 @@ def main():
             "index_bytes_per_step": index_bytes(cfg, args.staged, n_send, pad_rows),
             **({} if m == 1 else {"pad_multiple": m, "padding_rows": pad_rows}),
             "host_enqueue_us_per_step": round(host_us, 1),
+            "step_us": step_us,
+            **({} if per_pass is None else {"per_pass_us": per_pass}),
             "timing": ("hip graph replay" if graphs is not None else "eager launches") +
                       f", events: {args.events if graphs is None else 'none'}",
             **({} if not args.staged else {
@@ -746,6 +793,9 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": row_bytes[dom],
             "avg_launch_us": round(dom_us, 2),
+            "median_launch_us": round(med_us[dom], 2),
+            "achievable_copy_GBps": ceiling,
+            "frac_of_achievable": None if ceiling is None else round(achieved / ceiling, 4),
         },
         "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seconds, args.staged, m),
     }

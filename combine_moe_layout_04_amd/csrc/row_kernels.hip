@@ -279,13 +279,6 @@ __global__ __launch_bounds__(1024) void token_dot_kernel(DotArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst,
-                                                   const u32x4* __restrict__ src, size_t n) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) dst[i] = src[i];
-}
-
 // ---- launch geometry and template selection -----------------------------------
 
 int groups_per_token(int NV, int cpl) { return (NV + kWave * cpl - 1) / (kWave * cpl); }
@@ -385,16 +378,6 @@ hipError_t launch_gather(const GatherArgs& a, const Tuning& t, hipStream_t s) {
 
 hipError_t launch_token_dot(const DotArgs& a, const Tuning& t, hipStream_t s) {
   return a.dtype == kF32 ? dot_mode<kF32>(a, t, s) : dot_mode<kBF16>(a, t, s);
-}
-
-hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
-  const size_t n = bytes / 16;
-  if (n == 0) return hipSuccess;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), n);
-  return hipGetLastError();
 }
 
 }  // namespace moe
