@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) when no GPU is visible, so that a
-    # plain `pytest` on a CPU host stays green; `-m gpu` on the GPU machine runs them.
+    # plain `pytest` on a CPU host stays green; `-m gpu` on an MI355X host runs them.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
