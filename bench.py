@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--chunks-per-lane", type=int, default=0)
-    ap.add_argument("--nontemporal", type=int, default=1)
+    ap.add_argument("--nontemporal", type=int, default=2)
     ap.add_argument("--waves-per-block", type=int, default=0)
     ap.add_argument("--layout-pairs", type=int, default=0)
     ap.add_argument("--events", choices=["all", "dominant", "none"], default="dominant",

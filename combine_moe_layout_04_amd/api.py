@@ -83,7 +83,7 @@ def moe_workspace_size(T: int, K: int, E: int, P: int, pad_multiple: int = 1) ->
 class Handle:
     """Opaque layout handle plus the device workspace its arrays live in."""
 
-    def __init__(self, chunks_per_lane: int = 0, nontemporal: int = 1, waves_per_block: int = 0,
+    def __init__(self, chunks_per_lane: int = 0, nontemporal: int = 2, waves_per_block: int = 0,
                  layout_pairs: int = 0, pad_multiple: int = 1):
         tun = MoeTuning(chunks_per_lane, nontemporal, waves_per_block, layout_pairs)
         h = ctypes.c_void_p()

@@ -94,14 +94,15 @@ enum moe_field {
                                           (rows >= send_offset[P] unspecified)          */
 };
 
-/* Optional launch knobs; zero means "library default".  A row is cut into
- * 16-byte chunks and the chunks into segments of 64 (one wavefront access);
- * the row kernels run one wavefront per (token, segment group).           */
+/* Optional launch knobs; zero means "library default" except for
+ * nontemporal, whose default applies when the struct is NULL.  A row is cut
+ * into 16-byte chunks and the chunks into segments of 64 (one wavefront
+ * access); the row kernels run one wavefront per (token, segment group).   */
 typedef struct moe_tuning {
   int chunks_per_lane;  /* consecutive segments per wavefront, i.e. chunks of one row each
                            lane keeps in flight: 0 (= 1), 1, 2 or 4                        */
-  int nontemporal;      /* 0: default loads/stores; 1 (default): receive-row loads and
-                           stores marked non-temporal; 2: token-row stores too          */
+  int nontemporal;      /* 0: default loads/stores; 1: receive-row loads and stores
+                           marked non-temporal; 2 (default): token-row stores too    */
   int waves_per_block;  /* wavefronts per workgroup of the row kernels: 0 (= 4), 1, 2, 4, 8 */
   int layout_pairs;     /* (t,k) pairs per layout tile: 0 (= 512), 512, 1024, 2048, 4096      */
 } moe_tuning;
