@@ -54,16 +54,28 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"rows must be float32 or bfloat16, got {t.dtype}")
 
 
+# Argument marshalling is on every call's host path (a few microseconds per
+# call matter for small batches), so pointers and streams go to ctypes as
+# plain integers and devices are compared by index.
+
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device) -> int:
+    """torch's current stream on `device`, as a raw hipStream_t.  The raw
+    query returns the same stream as torch.cuda.current_stream(device)
+    (stream contexts included) in a few percent of its time."""
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _need(t: torch.Tensor, name: str, device, shape=None, dtype=None):
-    if not t.is_cuda or t.device != device:
+    if t.get_device() != device.index:  # -1 for a host tensor
         raise ValueError(f"{name} must be on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -78,6 +90,17 @@ def moe_workspace_size(T: int, K: int, E: int, P: int, pad_multiple: int = 1) ->
     _check(lib().moe_workspace_size_padded(T, K, E, P, pad_multiple, ctypes.byref(n)),
            "moe_workspace_size")
     return n.value
+
+
+_SIZES = {}  # (T, K, E, P, pad_multiple) -> workspace bytes (pure host functions of the shape)
+
+
+def _workspace_bytes(T, K, E, P, pad):
+    key = (T, K, E, P, pad)
+    v = _SIZES.get(key)
+    if v is None:
+        v = _SIZES[key] = moe_workspace_size(T, K, E, P, pad)
+    return v
 
 
 class Handle:
@@ -141,20 +164,21 @@ def moe_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
     T, K = topk_idx.shape
     E, P = int(num_experts), int(num_partitions)
     h = handle if handle is not None else Handle()
-    need = moe_workspace_size(T, K, E, P, h.pad_multiple)
     if workspace is None:
+        need = _workspace_bytes(T, K, E, P, h.pad_multiple)
         ws = h.workspace
-        if ws is None or ws.numel() < need or ws.device != dev:
+        if ws is None or ws.numel() < need or ws.get_device() != dev.index:
             ws = torch.empty(need, dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", dev, dtype=torch.uint8)
-        ws = workspace
+        ws = workspace  # the library checks its size
     _check(lib().moe_layout(h.ptr, _ptr(topk_idx), itype, T, K, E, P, _ptr(ws), ws.numel(),
                             _stream(dev)), "moe_layout")
+    if (h.T, h.K, h.E, h.P) != (T, K, E, P) or h.R is None:
+        n = ctypes.c_int64(0)
+        _check(lib().moe_recv_capacity(h.ptr, ctypes.byref(n)), "moe_recv_capacity")
+        h.R = n.value  # receive rows: T*K, plus the padding capacity of a padded handle
     h.workspace, h.T, h.K, h.E, h.P, h.device = ws, T, K, E, P, dev
-    n = ctypes.c_int64(0)
-    _check(lib().moe_recv_capacity(h.ptr, ctypes.byref(n)), "moe_recv_capacity")
-    h.R = n.value  # receive rows: T*K, plus the padding capacity of a padded handle
     return h
 
 
