@@ -183,7 +183,8 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   const int E1 = a.E + 1;
   const int NR = E1 + a.P;                   // histogram columns
   const int parts = max(1, min(a.nblk, kLT / NR));
-  int* base = reinterpret_cast<int*>(smem);  // [NR]   this tile's start of each column
+  unsigned long long* colm = reinterpret_cast<unsigned long long*>(smem);  // [P] tokens of the tile in partition r
+  int* base = reinterpret_cast<int*>(colm + a.P);  // [NR]   this tile's start of each column
   int* off = base + NR;                      // [NR+1] start of each column, tile 0
   int* cnt = off + NR + 1;                   // [kLW][E+1] per-wave bucket cursors
   int* wsum = cnt + kLW * E1;                // [kLW]
@@ -218,7 +219,8 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
 #pragma unroll
       for (int u = 0; u < kIdRegs; ++u) idv[u] = src[min(tid + u * kLT, np - 1)];
     }
-    m0 = a.tok_mask[t0 + min(tid, nt - 1)];
+    // a tile of at most 64 tokens: every wave holds token `lane`'s mask
+    m0 = a.tok_mask[t0 + min(nt <= kWave ? lane : tid, nt - 1)];
   }
   for (int r = tid; r < a.P; r += kLT) carry[r] = 0;
 
@@ -258,22 +260,32 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   __syncthreads();
 
   // 4. token send slots: per partition, a ballot over the tokens ranks them.
-  //    A tile of at most 64 tokens (the usual case) is one wave's work; a
-  //    larger one takes one token per thread per round, with a table of
+  //    A tile of at most 64 tokens (the usual case) takes one ballot per
+  //    partition, the partitions spread over the waves; a token's slot is
+  //    then the popcount of its partition's ballot below it, so the tile's
+  //    [tokens][P] block of token_slot is written contiguously (coalesced)
+  //    and send_token partition by partition (neighbouring send rows).  A
+  //    larger tile takes one token per thread per round, with a table of
   //    per-wave starts that places the waves
   if (nt <= kWave) {  // uniform
-    if (wv == 0) {
-      const unsigned long long m = lane < nt ? m0 : 0ull;
-#pragma unroll 4
-      for (int r = 0; r < a.P; ++r) {
-        const int on = (int)((m >> r) & 1ull);
-        const uint64_t bal = __ballot(on);
-        const int slot = base[E1 + r] - off[E1 + r] + __popcll(bal & lanes_below(lane));
-        if (lane < nt) {
-          a.token_slot[(size_t)(t0 + lane) * a.P + r] = on ? slot : -1;
-          if (on) a.send_token[off[E1 + r] - off[E1] + slot] = t0 + lane;
-        }
-      }
+    const unsigned long long m = lane < nt ? m0 : 0ull;
+    for (int r = wv; r < a.P; r += kLW) {
+      const uint64_t bal = __ballot((int)((m >> r) & 1ull));
+      if (lane == 0) colm[r] = bal;
+    }
+    __syncthreads();  // no global store is outstanding here
+    for (int i = tid; i < nt * a.P; i += kLT) {
+      const int tt = i / a.P;
+      const int r = i - tt * a.P;
+      const uint64_t bal = colm[r];
+      const int slot = base[E1 + r] - off[E1 + r] + __popcll(bal & lanes_below(tt));
+      a.token_slot[(size_t)t0 * a.P + i] = ((bal >> tt) & 1ull) ? slot : -1;
+    }
+    for (int i = tid; i < a.P * nt; i += kLT) {
+      const int r = i / nt;
+      const int tt = i - r * nt;
+      const uint64_t bal = colm[r];
+      if ((bal >> tt) & 1ull) a.send_token[base[E1 + r] - off[E1] + __popcll(bal & lanes_below(tt))] = t0 + tt;
     }
   } else {
   for (int c0 = 0; c0 < nt; c0 += kLT) {  // uniform
@@ -387,7 +399,7 @@ size_t layout_rank_lds(int E, int P, int tile, int K) {
   const size_t E1 = (size_t)E + 1, NR = E1 + P;
   const size_t parts_nr = NR > (size_t)kLT ? NR : (size_t)kLT;  // parts * NR <= max(kLT, NR)
   const size_t ints = NR + (NR + 1) + kLW * E1 + kLW + 2 * (size_t)kLW * P + P + NR + 2 * parts_nr;
-  return ints * 4 + (size_t)tile * K * 2;
+  return (size_t)P * 8 + ints * 4 + (size_t)tile * K * 2;
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
