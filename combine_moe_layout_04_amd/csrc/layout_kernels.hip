@@ -39,6 +39,11 @@ constexpr int kLT = kLayoutThreads;  // threads per layout workgroup
 constexpr int kLW = kLT / kWave;     // waves per layout workgroup
 constexpr int kColRegs = 64;         // histogram tiles a scan thread loads at once
 constexpr int kIdRegs = 2;           // tile ids a thread loads before the scan
+// token slots of a tile of at most 64 tokens: ballots per wave, and at most
+// this many rounds of the block over the tile's [tokens][P] items
+constexpr int kSlotBallots = (MOE_MAX_P + kLW - 1) / kLW;
+constexpr int kSlotRounds = (kWave * MOE_MAX_P + kLT - 1) / kLT;
+static_assert(kSlotRounds == 8, "the rank kernel's round switch covers 1..8 rounds");
 
 __device__ __forceinline__ int clamp_id(long long v, int E) { return (v >= 0 && v < E) ? (int)v : E; }
 
@@ -178,6 +183,49 @@ __device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int 
   __syncthreads();
 }
 
+// Token slots of a tile of at most 64 tokens, from colm[r] (the tile's
+// tokens in partition r, one bit per token): item i of the block is (token
+// i / P, partition i % P) for token_slot, a contiguous [tokens][P] block, and
+// (partition i / nt, token i % nt) for send_token, partition by partition.
+// NR rounds of kLT items, unrolled: both indices advance by kLT per round
+// without a division, every round's LDS reads are issued unconditionally
+// (clamped) and only the stores are guarded.
+template <int NR>
+__device__ __forceinline__ void write_slots(const LayoutArgs& a, const unsigned long long* colm, const int* base,
+                                            const int* off, int t0, int nt) {
+  const int tid = threadIdx.x;
+  const int E1 = a.E + 1;
+  const int nitems = nt * a.P;
+  const int ntd = max(nt, 1);
+  int tq = tid / a.P, tr = tid - (tid / a.P) * a.P;  // token-major
+  int sr = tid / ntd, st = tid - (tid / ntd) * ntd;  // partition-major
+  const int dq = kLT / a.P, dr = kLT - (kLT / a.P) * a.P;
+  const int ds = kLT / ntd, dt = kLT - (kLT / ntd) * ntd;
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int i = tid + j * kLT;
+    {  // past the items (i >= nitems) the token index is clamped, not stored
+      const int r = tr;
+      const int q = min(tq, kWave - 1);
+      const uint64_t bal = colm[r];
+      const int slot = base[E1 + r] - off[E1 + r] + __popcll(bal & lanes_below(q));
+      if (i < nitems) a.token_slot[(size_t)t0 * a.P + i] = ((bal >> q) & 1ull) ? slot : -1;
+    }
+    {
+      const int r = min(sr, a.P - 1);
+      const uint64_t bal = colm[r];
+      const int row = base[E1 + r] - off[E1] + __popcll(bal & lanes_below(st));
+      if (i < nitems && ((bal >> st) & 1ull)) a.send_token[row] = t0 + st;
+    }
+    tq += dq;
+    tr += dr;
+    if (tr >= a.P) { tr -= a.P; ++tq; }
+    sr += ds;
+    st += dt;
+    if (st >= ntd) { st -= ntd; ++sr; }
+  }
+}
+
 __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   extern __shared__ __align__(8) unsigned char smem[];
   const int E1 = a.E + 1;
@@ -269,23 +317,24 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   //    per-wave starts that places the waves
   if (nt <= kWave) {  // uniform
     const unsigned long long m = lane < nt ? m0 : 0ull;
-    for (int r = wv; r < a.P; r += kLW) {
-      const uint64_t bal = __ballot((int)((m >> r) & 1ull));
-      if (lane == 0) colm[r] = bal;
+#pragma unroll
+    for (int j = 0; j < kSlotBallots; ++j) {
+      const int r = wv + j * kLW;
+      if (r < a.P) {  // uniform
+        const uint64_t bal = __ballot((int)((m >> r) & 1ull));
+        if (lane == 0) colm[r] = bal;
+      }
     }
     __syncthreads();  // no global store is outstanding here
-    for (int i = tid; i < nt * a.P; i += kLT) {
-      const int tt = i / a.P;
-      const int r = i - tt * a.P;
-      const uint64_t bal = colm[r];
-      const int slot = base[E1 + r] - off[E1 + r] + __popcll(bal & lanes_below(tt));
-      a.token_slot[(size_t)t0 * a.P + i] = ((bal >> tt) & 1ull) ? slot : -1;
-    }
-    for (int i = tid; i < a.P * nt; i += kLT) {
-      const int r = i / nt;
-      const int tt = i - r * nt;
-      const uint64_t bal = colm[r];
-      if ((bal >> tt) & 1ull) a.send_token[base[E1 + r] - off[E1] + __popcll(bal & lanes_below(tt))] = t0 + tt;
+    switch ((nt * a.P + kLT - 1) / kLT) {  // uniform: rounds of the block over the tile's items
+      case 1: write_slots<1>(a, colm, base, off, t0, nt); break;
+      case 2: write_slots<2>(a, colm, base, off, t0, nt); break;
+      case 3: write_slots<3>(a, colm, base, off, t0, nt); break;
+      case 4: write_slots<4>(a, colm, base, off, t0, nt); break;
+      case 5: write_slots<5>(a, colm, base, off, t0, nt); break;
+      case 6: write_slots<6>(a, colm, base, off, t0, nt); break;
+      case 7: write_slots<7>(a, colm, base, off, t0, nt); break;
+      default: write_slots<kSlotRounds>(a, colm, base, off, t0, nt); break;
     }
   } else {
   for (int c0 = 0; c0 < nt; c0 += kLT) {  // uniform
