@@ -111,6 +111,36 @@ __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
 
 // ---- rank -------------------------------------------------------------------
 
+// Column sums of the histogram over the tile ranges of scan_histogram: item
+// (q, r) sums column r over tiles [q*cpp, (q+1)*cpp), in batches of L
+// clamped, unconditional loads (no branch waits on a load, so a batch is in
+// flight together); the total goes to part[q][r], the tiles before b to
+// part[parts + q][r].
+template <int L>
+__device__ __forceinline__ void column_sums(const int* __restrict__ h, int NR, int nblk, int b, int parts, int cpp,
+                                            int* part) {
+  for (int item = threadIdx.x; item < NR * parts; item += kLT) {
+    const int q = item / NR;
+    const int r = item - q * NR;
+    const int j0 = q * cpp;
+    const int j1 = min(nblk, j0 + cpp);
+    int tot = 0, pre = 0;
+    for (int c0 = j0; c0 < j1; c0 += L) {
+      int v[L];
+#pragma unroll
+      for (int u = 0; u < L; ++u) v[u] = h[(size_t)min(c0 + u, j1 - 1) * NR + r];
+#pragma unroll
+      for (int u = 0; u < L; ++u) {
+        const int x = (c0 + u < j1) ? v[u] : 0;
+        tot += x;
+        pre += (c0 + u < b) ? x : 0;
+      }
+    }
+    part[q * NR + r] = tot;
+    part[(parts + q) * NR + r] = pre;
+  }
+}
+
 // Start of every histogram column, globally and at tile b.  The histogram is
 // tile-major, h[j * NR + r]: count of column r (a bucket, then a partition)
 // in tile j.  Writes col_n[r] = column r's total, col_0[r] = sum of all
@@ -127,28 +157,23 @@ __device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int 
   const int wv = tid / kWave;
   const int parts = max(1, min(nblk, kLT / NR));  // threads per column
   const int cpp = (nblk + parts - 1) / parts;     // tiles per thread
-  for (int item = tid; item < NR * parts; item += kLT) {
-    const int q = item / NR;
-    const int r = item - q * NR;
-    const int j0 = q * cpp;
-    const int j1 = min(nblk, j0 + cpp);
-    int tot = 0, pre = 0;
-    for (int c0 = j0; c0 < j1; c0 += kColRegs) {
-      // clamped, unconditional loads: no branch waits on a load, so all of
-      // them are in flight together
-      int v[kColRegs];
-#pragma unroll
-      for (int u = 0; u < kColRegs; ++u) v[u] = h[(size_t)min(c0 + u, j1 - 1) * NR + r];
-#pragma unroll
-      for (int u = 0; u < kColRegs; ++u) {
-        const int x = (c0 + u < j1) ? v[u] : 0;
-        tot += x;
-        pre += (c0 + u < b) ? x : 0;
-      }
-    }
-    part[q * NR + r] = tot;
-    part[(parts + q) * NR + r] = pre;
-  }
+  // loads in flight per thread: the tiles it sums, rounded up a short ladder
+  if (cpp <= 4)
+    column_sums<4>(h, NR, nblk, b, parts, cpp, part);
+  else if (cpp <= 8)
+    column_sums<8>(h, NR, nblk, b, parts, cpp, part);
+  else if (cpp <= 12)
+    column_sums<12>(h, NR, nblk, b, parts, cpp, part);
+  else if (cpp <= 16)
+    column_sums<16>(h, NR, nblk, b, parts, cpp, part);
+  else if (cpp <= 24)
+    column_sums<24>(h, NR, nblk, b, parts, cpp, part);
+  else if (cpp <= 32)
+    column_sums<32>(h, NR, nblk, b, parts, cpp, part);
+  else if (cpp <= 48)
+    column_sums<48>(h, NR, nblk, b, parts, cpp, part);
+  else
+    column_sums<kColRegs>(h, NR, nblk, b, parts, cpp, part);
   __syncthreads();
   int carry = 0;
   for (int c0 = 0; c0 < NR; c0 += kLT) {  // uniform
