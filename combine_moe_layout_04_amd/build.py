@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_layout.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.hip", "layout_kernels.hip", "row_kernels.hip", "staged_kernels.hip", "pad_kernels.hip", "copy_kernels.hip"]
+SOURCES = ["abi.hip", "layout_kernels.hip", "row_kernels.hip", "staged_kernels.hip", "copy_kernels.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -107,9 +107,10 @@ int check_rows(const moe_handle_s* h, int dtype, int64_t H, int* NV) {
   if (H < 1 || (H * eb) % 16 != 0) return MOE_ERR_SHAPE;
   const int64_t nv = H * eb / 16;
   if (nv >= (int64_t(1) << 31) || nv * h->R >= (int64_t(1) << 62)) return MOE_ERR_UNSUPPORTED;
-  // one wave per (token, segment): the grid must fit in a 32-bit wave index
-  if (moe::row_waves(h->T, (int)nv, 1) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
-  if (h->pad > 1 && moe::pad_fill_waves(h->E, h->pad, (int)nv) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  // one wave per (token, segment), then the padding waves: the grid must fit
+  // in a 32-bit wave index
+  if (moe::row_waves(h->T, (int)nv, 1) + moe::pad_fill_waves(h->E, h->pad, (int)nv) > INT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
   *NV = (int)nv;
   return MOE_OK;
 }
@@ -129,9 +130,13 @@ T* ws_ptr(const moe_handle_s* h, size_t off) {
 
 // Padded layouts: zero rows (and zero scores) in the padding of every expert
 // segment of a receive buffer the call just wrote.  Nothing when unpadded.
-int fill_padding(const moe_handle_s* h, void* rows, float* scores, int NV, hipStream_t stream) {
-  if (h->pad <= 1) return MOE_OK;
+// The padding rows a call writes into a padded receive buffer (zero rows and
+// zero scores): filled by extra waves of the call's row kernel.  pad = 1 (an
+// unpadded handle) adds no wave.
+moe::PadArgs pad_rows(const moe_handle_s* h, void* rows, float* scores, int NV) {
   moe::PadArgs p{};
+  p.pad = 1;
+  if (h->pad <= 1) return p;
   p.dst = rows;
   p.scores_out = scores;
   p.expert_offset = ws_ptr<int>(h, h->plan.expert_offset);
@@ -140,7 +145,10 @@ int fill_padding(const moe_handle_s* h, void* rows, float* scores, int NV, hipSt
   p.NV = NV;
   p.R = (int)h->R;
   p.pad = h->pad;
-  return hip_status(moe::launch_pad_fill(p, h->tune, stream));
+  p.ngrp = (NV + 63) / 64;
+  p.nblk = (h->pad - 1 + moe::kPadRows - 1) / moe::kPadRows;
+  p.nwaves = (int)moe::pad_fill_waves(h->E, h->pad, NV);  // fits: checked with the row waves
+  return p;
 }
 
 }  // namespace
@@ -281,8 +289,8 @@ int moe_dispatch(moe_handle_t h, const void* x, int dtype, int64_t H, const floa
   a.dtype = dtype;
   a.scale = scale_rows != 0;
   a.status = ws_ptr<int>(h, h->plan.status);
-  const int rc = hip_status(moe::launch_scatter(a, h->tune, stream));
-  return rc != MOE_OK ? rc : fill_padding(h, recv, recv_scores, NV, stream);
+  a.pad = pad_rows(h, recv, recv_scores, NV);
+  return hip_status(moe::launch_scatter(a, h->tune, stream));
 }
 
 int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H, const float* topk_weights,
@@ -336,8 +344,8 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   a.dtype = dtype;
   a.scale = topk_weights != nullptr;
   a.status = ws_ptr<int>(h, h->plan.status);
+  a.pad = pad_rows(h, grad_y, nullptr, NV);  // no gradient in the padding rows
   st = grad_y ? hip_status(moe::launch_scatter(a, h->tune, stream)) : MOE_OK;
-  if (st == MOE_OK && grad_y) st = fill_padding(h, grad_y, nullptr, NV, stream);  // no gradient there
   if (st != MOE_OK || !grad_w) return st;
   // router-weight gradient: a separate pass over grad_out and y (measured
   // faster than fusing it into the row stores: HBM turns around less)
@@ -429,7 +437,8 @@ int staged_args(const moe_handle_s* h, int dtype, int64_t H, int64_t send_rows, 
   if (st != MOE_OK) return st;
   const int64_t cap = h->T * (h->K < h->P ? h->K : h->P);
   if (send_rows < cap) return MOE_ERR_SHAPE;
-  if (cap * (int64_t)((NV + 63) / 64) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (cap * (int64_t)((NV + 63) / 64) + moe::pad_fill_waves(h->E, h->pad, NV) > INT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
   *a = moe::StagedArgs{};
   a->recv_pos = ws_ptr<int>(h, h->plan.recv_pos);
   a->token_slot = ws_ptr<int>(h, h->plan.token_slot);
@@ -483,8 +492,8 @@ int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t s
   a.w = topk_weights;
   a.scores_out = recv_scores;
   a.scale = scale_rows != 0;
-  const int rc = hip_status(moe::launch_expand(a, h->tune, stream));
-  return rc != MOE_OK ? rc : fill_padding(h, recv, recv_scores, a.NV, stream);
+  a.pad = pad_rows(h, recv, recv_scores, a.NV);
+  return hip_status(moe::launch_expand(a, h->tune, stream));
 }
 
 int moe_reduce_partitions(moe_handle_t h, const void* y, int dtype, int64_t H,

@@ -60,6 +60,30 @@ size_t layout_rank_lds(int E, int P, int tile, int K);
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
 
+// Padding rows of a padded layout: rows [expert_offset[e] + n_e,
+// expert_offset[e+1]) of every expert get zero chunks (and a zero score).
+// Written by extra waves of the kernel that writes the receive rows.
+constexpr int kPadRows = 8;  // padding rows per fill wave
+
+struct PadArgs {
+  void* dst;                         // [R, NV] chunks
+  float* scores_out;                 // [R] or null
+  const int* expert_offset;          // [E+1], padded
+  const int* num_tokens_per_expert;  // [E]
+  int E, NV, R;
+  int pad;                           // the handle's multiple (1: no padding, no fill waves)
+  int ngrp;                          // segments per row
+  int nblk;                          // row blocks per expert
+  int nwaves;                        // fill waves: pad_fill_waves(E, pad, NV), 0 when unpadded
+};
+
+// Wavefronts of one padding fill: an expert has at most pad-1 padding rows,
+// in blocks of kPadRows, and a row has one segment per 64 chunks.
+inline int64_t pad_fill_waves(int E, int pad, int NV) {
+  if (pad <= 1) return 0;
+  return (int64_t)E * ((pad - 1 + kPadRows - 1) / kPadRows) * ((NV + 63) / 64);
+}
+
 // Token-row -> receive-row direction (dispatch, rows of the combine backward).
 struct ScatterArgs {
   const void* src;        // [T, NV] chunks
@@ -72,6 +96,7 @@ struct ScatterArgs {
   int dtype;
   bool scale;             // dst = round(w * src)
   int* status;
+  PadArgs pad;            // padding rows of dst, filled by pad.nwaves waves after the token waves
 };
 
 // Receive-row -> token-row direction (combine, unscaled dispatch backward).
@@ -120,6 +145,7 @@ struct StagedArgs {
   int dtype;
   bool scale;             // expand: dst = round(w * src)
   int* status;
+  PadArgs pad;            // expand: padding rows of dst, filled by the grid's first pad.nwaves waves
 };
 
 struct Tuning {
@@ -143,22 +169,5 @@ hipError_t launch_expand(const StagedArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_reduce_partitions(const StagedArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_combine_partitions(const StagedArgs& a, const Tuning& t, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
-
-// Padding rows of a padded layout: rows [expert_offset[e] + n_e,
-// expert_offset[e+1]) of every expert get zero chunks (and a zero score).
-struct PadArgs {
-  void* dst;                         // [R, NV] chunks
-  float* scores_out;                 // [R] or null
-  const int* expert_offset;          // [E+1], padded
-  const int* num_tokens_per_expert;  // [E]
-  int E, NV, R;
-  int pad;                           // the handle's multiple: at most pad-1 padding rows per expert
-  int ngrp;                          // segments per row (set by the launcher)
-  int nblk;                          // row blocks per expert (set by the launcher)
-};
-
-// Wavefronts of one padding fill (its wave index must fit in 32 bits).
-int64_t pad_fill_waves(int E, int pad, int NV);
-hipError_t launch_pad_fill(const PadArgs& a, const Tuning& t, hipStream_t s);
 
 }  // namespace moe

@@ -5,25 +5,32 @@
 // GEMM over the padded segments then reads zeros, and its weight gradient
 // gets nothing from them.
 //
-// One wavefront per (expert, block of kPadRows padding rows, segment of 64
-// chunks): it stores one zero chunk per lane and row of its block, so a
-// segment's padding is written by many waves at once.  The wave of segment 0
-// also clears the block's scores, one row per lane.
+// The fill is not a launch of its own: the kernel that writes a call's
+// receive rows adds pad_fill_waves(E, pad, NV) wavefronts to its grid, and
+// each of them runs pad_fill_wave.  The scatter puts them after its token
+// waves, where they overlap its drain; the staged expansion puts them first,
+// because the end of its grid is send-row waves past N_send that exit at once
+// (its grid is sized for the worst case), behind which the fill would run
+// alone.  The padding rows and the pair rows are disjoint, so the two
+// kinds of wave never touch the same row.  One fill wave per (expert, block of
+// kPadRows padding rows, segment of 64 chunks): it stores one zero chunk per
+// lane and row of its block, and the wave of segment 0 also clears the
+// block's scores, one row per lane.
+#pragma once
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace moe {
-namespace {
 
-constexpr int kPadRows = 8;  // padding rows per wave
-
-__global__ __launch_bounds__(512) void pad_fill_kernel(PadArgs a) {
+// Wave w of the fill (0 <= w < pad_fill_waves(E, pad, NV); waves past the
+// last expert return at once).
+__device__ __forceinline__ void pad_fill_wave(const PadArgs& a, int w) {
   const int lane = lane_id();
-  const int gw = blockIdx.x * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
   const int per_e = a.nblk * a.ngrp;  // waves per expert
-  const int e = gw / per_e;
+  const int e = w / per_e;
   if (e >= a.E) return;  // wave-uniform
-  const int rem = gw - e * per_e;
+  const int rem = w - e * per_e;
   const int rb = rem / a.ngrp;
   const int grp = rem - rb * a.ngrp;
   const int seg_end = min(a.expert_offset[e + 1], a.R);  // never past the buffer
@@ -38,23 +45,6 @@ __global__ __launch_bounds__(512) void pad_fill_kernel(PadArgs a) {
       if (lo + i < hi) store_chunk<true>(dst + (size_t)(lo + i) * a.NV + j, zero);
   }
   if (grp == 0 && a.scores_out && lane < kPadRows && lo + lane < hi) a.scores_out[lo + lane] = 0.f;
-}
-
-}  // namespace
-
-int64_t pad_fill_waves(int E, int pad, int NV) {
-  // an expert has at most pad-1 padding rows
-  return (int64_t)E * ((pad - 1 + kPadRows - 1) / kPadRows) * ((NV + kWave - 1) / kWave);
-}
-
-hipError_t launch_pad_fill(const PadArgs& a0, const Tuning& t, hipStream_t s) {
-  PadArgs a = a0;
-  a.ngrp = (a.NV + kWave - 1) / kWave;
-  a.nblk = (a.pad - 1 + kPadRows - 1) / kPadRows;
-  const int wpb = t.waves_per_block;
-  const int64_t waves = pad_fill_waves(a.E, a.pad, a.NV);
-  hipLaunchKernelGGL(pad_fill_kernel, dim3((unsigned)((waves + wpb - 1) / wpb)), dim3(wpb * kWave), 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace moe

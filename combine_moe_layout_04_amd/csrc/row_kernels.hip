@@ -27,6 +27,7 @@
 // bad one raises MOE_STATUS_BAD_POSITION and the row is skipped.
 #include "device_common.h"
 #include "internal.h"
+#include "pad_fill.h"
 #include "../../include/moe_layout.h"
 
 namespace moe {
@@ -70,7 +71,11 @@ __global__ __launch_bounds__(512) void scatter_kernel(ScatterArgs a) {
   const int wpb = blockDim.x / kWave;
   const int gw = blockIdx.x * wpb + (int)(threadIdx.x / kWave);
   const int t = gw / a.ngrp;
-  if (t >= a.T) return;  // wave-uniform
+  if (t >= a.T) {  // wave-uniform: the padding waves follow the token waves
+    const int w = gw - a.T * a.ngrp;
+    if (w < a.pad.nwaves) pad_fill_wave(a.pad, w);
+    return;
+  }
   const int grp = gw - t * a.ngrp;
   const int jb = grp * kWave * CPL + lane;  // this lane's first chunk
 
@@ -288,7 +293,7 @@ hipError_t go_scatter(const ScatterArgs& a0, const Tuning& tu, hipStream_t s) {
   ScatterArgs a = a0;
   a.ngrp = groups_per_token(a.NV, CPL);
   const int wpb = tu.waves_per_block;
-  const int64_t waves = (int64_t)a.T * a.ngrp;
+  const int64_t waves = (int64_t)a.T * a.ngrp + a.pad.nwaves;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb)), block(wpb * kWave);
   if (tu.nontemporal >= 1)
     hipLaunchKernelGGL((scatter_kernel<DT, CPL, SCALE, true>), grid, block, 0, s, a);

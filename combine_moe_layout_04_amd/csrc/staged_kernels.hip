@@ -22,6 +22,7 @@
 // is bounds-checked and a bad one raises MOE_STATUS_BAD_POSITION.
 #include "device_common.h"
 #include "internal.h"
+#include "pad_fill.h"
 #include "../../include/moe_layout.h"
 
 namespace moe {
@@ -103,7 +104,12 @@ template <int DT, bool SCALE, bool NT>
 __global__ __launch_bounds__(512) void expand_kernel(StagedArgs a) {
   constexpr int V = Elems<DT>::kPerChunk;
   const int lane = lane_id();
-  const int gw = blockIdx.x * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
+  int gw = blockIdx.x * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
+  if (gw < a.pad.nwaves) {  // wave-uniform: the padding waves come first
+    pad_fill_wave(a.pad, gw);
+    return;
+  }
+  gw -= a.pad.nwaves;
   const int s = gw / a.ngrp;
   if (s >= a.send_cap) return;  // wave-uniform
   const int grp = gw - s * a.ngrp;
@@ -242,8 +248,8 @@ __global__ __launch_bounds__(512) void combine_partitions_kernel(StagedArgs a) {
 
 int segments(int NV) { return (NV + kWave - 1) / kWave; }
 
-dim3 grid_for(int64_t rows, int ngrp, int wpb) {
-  const int64_t waves = rows * ngrp;
+dim3 grid_for(int64_t rows, int ngrp, int wpb, int64_t extra_waves = 0) {
+  const int64_t waves = rows * ngrp + extra_waves;
   return dim3((unsigned)((waves + wpb - 1) / wpb));
 }
 
@@ -261,7 +267,8 @@ hipError_t go_send(StagedArgs a, const Tuning& tu, hipStream_t s) {
 template <int DT>
 hipError_t go_expand(StagedArgs a, const Tuning& tu, hipStream_t s) {
   a.ngrp = segments(a.NV);
-  const dim3 grid = grid_for(a.send_cap, a.ngrp, tu.waves_per_block), block(tu.waves_per_block * kWave);
+  const dim3 grid = grid_for(a.send_cap, a.ngrp, tu.waves_per_block, a.pad.nwaves),
+             block(tu.waves_per_block * kWave);
   const bool nt = tu.nontemporal >= 1;
   if (a.scale) {
     if (nt) hipLaunchKernelGGL((expand_kernel<DT, true, true>), grid, block, 0, s, a);
