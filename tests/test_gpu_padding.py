@@ -144,7 +144,8 @@ def test_padded_ragged(name, over, m):
 
 
 @pytest.mark.parametrize("tuning", [dict(layout_pairs=4096, waves_per_block=1),
-                                    dict(layout_pairs=2048, chunks_per_lane=2, waves_per_block=8)])
+                                    dict(layout_pairs=2048, chunks_per_lane=2, waves_per_block=8),
+                                    dict(chunks_per_lane=4, waves_per_block=2, nontemporal=0)])
 def test_padded_layout_tunings(tuning):
     cfg = W.get_config("qwen3_30b_a3b", T=3001)
     say(f"padded tunings {tuning}")
