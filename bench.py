@@ -55,9 +55,15 @@ def parse():
     ap.add_argument("--nontemporal", type=int, default=2)
     ap.add_argument("--waves-per-block", type=int, default=0)
     ap.add_argument("--layout-pairs", type=int, default=0)
-    ap.add_argument("--events", choices=["all", "dominant", "none"], default="dominant",
-                    help="HIP events in the timed region: around every call, around the "
-                         "dominant kernel's call only, or none")
+    ap.add_argument("--events", choices=["kernel", "all", "none"], default="kernel",
+                    help="HIP events in the timed region. kernel: the dominant kernel's own start and "
+                         "stop on every --kernel-every-th step, and a free stop event bound to each "
+                         "step's last kernel (step times); all: also hipEventRecord around every call, "
+                         "and the dominant kernel timed on every step (diagnostic: the records cost "
+                         "GPU time); none: wall time only")
+    ap.add_argument("--kernel-every", type=int, default=8,
+                    help="with --events kernel, time the dominant kernel on every n-th timed step "
+                         "(its start event is a stream marker: about 3 us of GPU time)")
     ap.add_argument("--staged", action="store_true",
                     help="staged exchange: send buffer per destination partition, receiver-side "
                          "expansion, two-level combine")
@@ -180,8 +186,10 @@ def index_bytes(cfg, staged=False, n_send=None, pad_rows=None):
 # The call whose kernel the roofline reports: the K-row gather-reduce (in the
 # staged exchange, its receiver-side half).
 DOMINANT = {False: "combine", True: "combine:reduce"}
-KERNEL_SOURCES = {False: ("row_kernels.hip", "device_common.h"),
-                  True: ("staged_kernels.hip", "device_common.h")}
+# what the committed traffic counters describe: the dominant kernel's
+# function, its launcher, and the device helpers it uses
+KERNEL_SOURCES = {False: ("row_kernels.hip", ("gather_kernel", "go_gather")),
+                  True: ("staged_kernels.hip", ("reduce_partitions_kernel", "go_reduce"))}
 
 
 def dominant_call(cfg, staged=False):
@@ -191,12 +199,27 @@ def dominant_call(cfg, staged=False):
     return name.replace("combine", "combine.0", 1)
 
 
+def function_text(src, name):
+    """Source text of the function `name` in `src`: from the template line
+    before its definition to the closing brace in column 0."""
+    m = re.search(r"^template <[^\n]*>\n(?:__global__[^\n]*|hipError_t) %s\(" % re.escape(name), src, re.M)
+    if m is None:
+        raise ValueError(f"{name} not found")
+    end = src.index("\n}\n", m.start())
+    return src[m.start():end + 3]
+
+
 def kernel_source_hash(staged=False):
-    """Hash of the sources of the dominant kernel (the counters' subject)."""
+    """Hash of the dominant kernel's source (the counters' subject): its
+    function, its launcher and device_common.h."""
+    csrc = os.path.join(ROOT, "combine_moe_layout_04_amd", "csrc")
+    path, funcs = KERNEL_SOURCES[staged]
+    src = open(os.path.join(csrc, path)).read()
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[staged]:
-        with open(os.path.join(ROOT, "combine_moe_layout_04_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in funcs:
+        h.update(function_text(src, f).encode())
+    with open(os.path.join(csrc, "device_common.h"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -605,17 +628,29 @@ def main():
         else:
             raise ValueError(kind)
 
-    def step(s, base=None):
-        # base: first event index of this step (events bracket the timed calls)
+    def step(s, i=None):
+        # i: timed step index.  On a timed step the dominant call's kernel
+        # may record its own start and stop, the last call's kernel binds the
+        # step's stop event, and with --events all every call is bracketed.
         for j, (_, kind, p, _) in enumerate(calls):
-            slot = None if base is None else slot_of.get(j)
-            if slot is not None:
-                hev.record(base + 2 * slot, stream)
+            slot = None
+            if i is not None:
+                h = s["pass"][p]["h"]
+                if j == d and i in kslot:
+                    r = kslot[i]
+                    M.moe_time_next_kernel(h, kev.ev[2 * r].value, kev.ev[2 * r + 1].value)
+                if j == ncall - 1 and bev is not None:
+                    M.moe_time_next_kernel(h, None, bev.ev[i].value)
+                slot = slot_of.get(j)
+                if slot is not None:
+                    hev.record(per_step * i + 2 * slot, stream)
             run_call(s, kind, p)
             if slot is not None:
-                hev.record(base + 2 * slot + 1, stream)
+                hev.record(per_step * i + 2 * slot + 1, stream)
 
-    slot_of = {}
+    slot_of, kslot, bev = {}, {}, None
+    d = names.index(dom)
+    assert d != ncall - 1, "the step's last call carries the step-boundary event"
     for i in range(args.warmup):
         step(sets[i % nsets])
     for s in sets:
@@ -646,25 +681,32 @@ def main():
         torch.cuda.synchronize()
 
     K = args.steps
-    d = names.index(dom)
-    timed = [] if graphs is not None or args.events == "none" else (
-        list(range(ncall)) if args.events == "all" else [d])
+    eager = graphs is None
+    events = args.events if eager else "none"
+    # --events all: hipEventRecord around every call
+    timed = list(range(ncall)) if events == "all" else []
     slot_of = {j: r for r, j in enumerate(timed)}
     per_step = 2 * len(timed)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     hev = HipEvents(per_step * K)
-    step_events = args.events != "none"
-    sev = HipEvents(K + 1 if step_events else 0)  # step boundaries
+    # the dominant kernel's own start and stop, on a sample of the timed steps
+    every = 1 if events == "all" else max(1, args.kernel_every)
+    ksteps = [i for i in range(K) if i % every == 0] if events != "none" else []
+    kslot = {i: r for r, i in enumerate(ksteps)}
+    kev = HipEvents(2 * len(ksteps))
+    # step boundaries: a stop event bound to each step's last kernel (free),
+    # or, for graph replays, a record after each replay
+    bev = HipEvents(K) if events != "none" else None
+    sev = HipEvents(K + 1 if not eager else 0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        if step_events:
+        if not eager:
             sev.record(i, stream)
-        if graphs is not None:
             graphs[i % nsets].replay()
         else:
-            step(sets[i % nsets], per_step * i)
-    if step_events:
+            step(sets[i % nsets], i)
+    if not eager:
         sev.record(K, stream)
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
@@ -672,17 +714,24 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / K
     host_us = (t_enq - t0) * 1e6 / K
 
-    # per-call event times (only the calls bracketed in the timed region)
+    # per-call event times (--events all only)
     call_ms = {names[j]: [hev.elapsed_ms(per_step * i + 2 * r, per_step * i + 2 * r + 1) for i in range(K)]
                for r, j in enumerate(timed)}
     hev.close()
+    kern_us = [kev.elapsed_ms(2 * r, 2 * r + 1) * 1e3 for r in range(len(ksteps))] or None
+    kev.close()
     avg_us = {n: float(np.mean(v)) * 1e3 for n, v in call_ms.items()}
     med_us = {n: float(np.median(v)) * 1e3 for n, v in call_ms.items()}
-    step_us = None
-    if step_events:
+    st = None
+    if bev is not None and K > 1:   # end of step i-1's last kernel to end of step i's
+        st = np.array([bev.elapsed_ms(i - 1, i) for i in range(1, K)]) * 1e3
+    elif not eager:
         st = np.array([sev.elapsed_ms(i, i + 1) for i in range(K)]) * 1e3
-        step_us = {"median": round(float(np.median(st)), 2), "p10": round(float(np.percentile(st, 10)), 2),
-                   "p90": round(float(np.percentile(st, 90)), 2)}
+    step_us = None if st is None else {
+        "median": round(float(np.median(st)), 2), "p10": round(float(np.percentile(st, 10)), 2),
+        "p90": round(float(np.percentile(st, 90)), 2)}
+    if bev is not None:
+        bev.close()
     sev.close()
     per_pass = None
     if cfg.absorbed and len(avg_us) == ncall:
@@ -724,7 +773,10 @@ def main():
     row_bytes = {n: b for n, _, _, b in calls}
     step_b = sum(row_bytes.values())
     value = step_b / (ms_per_step * 1e-3) / 1e9
-    dom_us = avg_us.get(dom)
+    # the dominant kernel's duration: its own start and stop events
+    # (hipExtLaunchKernel), which leave out the launch latency that the events
+    # around the call include
+    dom_us = None if kern_us is None else float(np.mean(kern_us))
     achieved = None if dom_us is None else row_bytes[dom] / (dom_us * 1e-6) / 1e9
     traffic = traffic_from_profiles(cfg, args.staged)
     direct_b = sum(b for _, _, _, b in step_calls(cfg))
@@ -766,7 +818,8 @@ def main():
             "step_us": step_us,
             **({} if per_pass is None else {"per_pass_us": per_pass}),
             "timing": ("hip graph replay" if graphs is not None else "eager launches") +
-                      f", events: {args.events if graphs is None else 'none'}",
+                      f", events: {events}" + (f" (dominant kernel timed on {len(ksteps)} of {K} steps)"
+                                               if ksteps else ""),
             **({} if not args.staged else {
                 "exchange": "staged",
                 "n_send": n_send,
@@ -793,7 +846,10 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": row_bytes[dom],
             "avg_launch_us": round(dom_us, 2),
-            "median_launch_us": round(med_us[dom], 2),
+            "median_launch_us": round(float(np.median(kern_us)), 2),
+            "launch_timing": f"the kernel's own start and stop events (hipExtLaunchKernel), on {len(ksteps)} "
+                             f"of the {K} timed steps",
+            **({} if dom not in avg_us else {"call_interval_avg_us": round(avg_us[dom], 2)}),
             "achievable_copy_GBps": ceiling,
             "frac_of_achievable": None if ceiling is None else round(achieved / ceiling, 4),
         },

@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     Handle,
     MoeError,
     moe_bench_copy,
+    moe_time_next_kernel,
     moe_combine,
     moe_combine_bwd,
     moe_dispatch,

@@ -50,6 +50,7 @@ SIGNATURES = {
                                 ctypes.POINTER(c_int), ctypes.POINTER(c_int)]),
     "moe_handle_check": (c_int, [c_void_p, c_void_p, ctypes.POINTER(c_int)]),
     "moe_bench_copy": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_time_next_kernel": (c_int, [c_void_p, c_void_p, c_void_p]),
     "moe_stream_create_cu_budget": (c_int, [c_int, c_int, ctypes.POINTER(c_void_p)]),
     "moe_stream_destroy": (c_int, [c_void_p]),
     "moe_strerror": (c_char_p, [c_int]),

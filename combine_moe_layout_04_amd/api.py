@@ -428,6 +428,14 @@ class CuBudgetStream:
             pass
 
 
+def moe_time_next_kernel(h: Handle, start: Optional[int], stop: Optional[int]) -> None:
+    """Measurement hook: the next kernel a row call on ``h`` launches binds
+    the raw ``hipEvent_t`` handle ``stop`` (an integer) to its completion
+    and, when ``start`` is given, records ``start`` just before it.
+    One-shot; ``None, None`` disarms."""
+    _check(lib().moe_time_next_kernel(h.ptr, start, stop), "moe_time_next_kernel")
+
+
 def moe_bench_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     """Plain device copy (calibration kernel for HBM traffic counters)."""
     if dst.numel() * dst.element_size() != src.numel() * src.element_size():

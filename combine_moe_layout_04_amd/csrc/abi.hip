@@ -17,6 +17,8 @@ struct moe_handle_s {
   char* ws = nullptr;
   moe::WsLayout plan{};
   moe::Tuning tune{};
+  hipEvent_t ev_start = nullptr;  // moe_time_next_kernel: for the next kernel launch only
+  hipEvent_t ev_stop = nullptr;
 };
 
 namespace moe {
@@ -77,6 +79,16 @@ WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs, int pa
 namespace {
 
 bool valid_handle(const moe_handle_s* h) { return h && h->magic == moe_handle_s::kMagic; }
+
+// The tuning of a kernel launch: the handle's, plus the events armed by
+// moe_time_next_kernel, which this launch takes (so no later one records them).
+moe::Tuning take_tuning(moe_handle_s* h) {
+  moe::Tuning t = h->tune;
+  t.ev_start = h->ev_start;
+  t.ev_stop = h->ev_stop;
+  h->ev_start = h->ev_stop = nullptr;
+  return t;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -290,7 +302,7 @@ int moe_dispatch(moe_handle_t h, const void* x, int dtype, int64_t H, const floa
   a.scale = scale_rows != 0;
   a.status = ws_ptr<int>(h, h->plan.status);
   a.pad = pad_rows(h, recv, recv_scores, NV);
-  return hip_status(moe::launch_scatter(a, h->tune, stream));
+  return hip_status(moe::launch_scatter(a, take_tuning(h), stream));
 }
 
 int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H, const float* topk_weights,
@@ -313,7 +325,7 @@ int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H, const float
   a.R = (int)h->R;
   a.dtype = dtype;
   a.status = ws_ptr<int>(h, h->plan.status);
-  return hip_status(moe::launch_gather(a, h->tune, stream));
+  return hip_status(moe::launch_gather(a, take_tuning(h), stream));
 }
 
 int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
@@ -345,7 +357,7 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   a.scale = topk_weights != nullptr;
   a.status = ws_ptr<int>(h, h->plan.status);
   a.pad = pad_rows(h, grad_y, nullptr, NV);  // no gradient in the padding rows
-  st = grad_y ? hip_status(moe::launch_scatter(a, h->tune, stream)) : MOE_OK;
+  st = grad_y ? hip_status(moe::launch_scatter(a, take_tuning(h), stream)) : MOE_OK;
   if (st != MOE_OK || !grad_w) return st;
   // router-weight gradient: a separate pass over grad_out and y (measured
   // faster than fusing it into the row stores: HBM turns around less)
@@ -362,7 +374,7 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   d.dtype = dtype;
   d.gather = false;
   d.status = a.status;
-  return hip_status(moe::launch_token_dot(d, h->tune, stream));
+  return hip_status(moe::launch_token_dot(d, take_tuning(h), stream));
 }
 
 int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H,
@@ -396,7 +408,7 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
     d.dtype = dtype;
     d.gather = grad_x != nullptr;  // without grad_x: the score gradient only
     d.status = ws_ptr<int>(h, h->plan.status);
-    return hip_status(moe::launch_token_dot(d, h->tune, stream));
+    return hip_status(moe::launch_token_dot(d, take_tuning(h), stream));
   }
   moe::GatherArgs a{};
   a.src = grad_recv;
@@ -409,7 +421,7 @@ int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H
   a.R = (int)h->R;
   a.dtype = dtype;
   a.status = ws_ptr<int>(h, h->plan.status);
-  return hip_status(moe::launch_gather(a, h->tune, stream));
+  return hip_status(moe::launch_gather(a, take_tuning(h), stream));
 }
 
 int moe_recv_capacity(moe_handle_t h, int64_t* rows) {
@@ -471,7 +483,7 @@ int moe_send(moe_handle_t h, const void* x, int dtype, int64_t H, void* send, in
   if (!aligned(x, 16) || !aligned(send, 16)) return MOE_ERR_ALIGNMENT;
   a.src = x;
   a.dst = send;
-  return hip_status(moe::launch_send(a, h->tune, stream));
+  return hip_status(moe::launch_send(a, take_tuning(h), stream));
 }
 
 int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t send_rows,
@@ -493,7 +505,7 @@ int moe_expand(moe_handle_t h, const void* send, int dtype, int64_t H, int64_t s
   a.scores_out = recv_scores;
   a.scale = scale_rows != 0;
   a.pad = pad_rows(h, recv, recv_scores, a.NV);
-  return hip_status(moe::launch_expand(a, h->tune, stream));
+  return hip_status(moe::launch_expand(a, take_tuning(h), stream));
 }
 
 int moe_reduce_partitions(moe_handle_t h, const void* y, int dtype, int64_t H,
@@ -509,7 +521,7 @@ int moe_reduce_partitions(moe_handle_t h, const void* y, int dtype, int64_t H,
   a.src = y;
   a.dst = partial;
   a.w = topk_weights;
-  return hip_status(moe::launch_reduce_partitions(a, h->tune, stream));
+  return hip_status(moe::launch_reduce_partitions(a, take_tuning(h), stream));
 }
 
 int moe_combine_partitions(moe_handle_t h, const void* partial, int dtype, int64_t H,
@@ -522,7 +534,7 @@ int moe_combine_partitions(moe_handle_t h, const void* partial, int dtype, int64
   if (!aligned(partial, 16) || !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
   a.src = partial;
   a.dst = out;
-  return hip_status(moe::launch_combine_partitions(a, h->tune, stream));
+  return hip_status(moe::launch_combine_partitions(a, take_tuning(h), stream));
 }
 
 int moe_handle_field(moe_handle_t h, int field, void** dev_ptr, size_t* bytes) {
@@ -601,6 +613,14 @@ int moe_stream_create_cu_budget(int cu_first, int cu_count, hipStream_t* out) {
 int moe_stream_destroy(hipStream_t stream) {
   if (!stream) return MOE_ERR_INVALID_ARG;
   return hip_status(hipStreamDestroy(stream));
+}
+
+int moe_time_next_kernel(moe_handle_t h, hipEvent_t start, hipEvent_t stop) {
+  if (!valid_handle(h)) return MOE_ERR_INVALID_ARG;
+  if (start && !stop) return MOE_ERR_INVALID_ARG;
+  h->ev_start = start;
+  h->ev_stop = stop;
+  return MOE_OK;
 }
 
 const char* moe_strerror(int status) {

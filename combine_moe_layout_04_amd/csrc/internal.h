@@ -1,6 +1,7 @@
 // Internal interface between the C ABI (abi.hip) and the kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -153,7 +154,24 @@ struct Tuning {
   int nontemporal;      // 0, 1, 2
   int waves_per_block;  // 1, 2, 4, 8
   int layout_pairs;     // 512, 1024, 2048, 4096
+  // measurement: when ev_stop is set, the launch goes through
+  // hipExtLaunchKernel, which binds ev_stop to the kernel's completion and,
+  // when ev_start is set too, records ev_start just before the kernel; null
+  // for every other launch
+  hipEvent_t ev_start = nullptr;
+  hipEvent_t ev_stop = nullptr;
 };
+
+// Launches a row kernel, with the tuning's measurement events when it has
+// them.
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, const Tuning& t,
+                          Args... args) {
+  if (t.ev_stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t.ev_start, t.ev_stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 constexpr int kMaxDotWaves = 16;         // waves of one token-dot workgroup
 constexpr size_t kMaxDotLds = 64 * 1024;  // LDS for its per-segment values

@@ -296,9 +296,9 @@ hipError_t go_scatter(const ScatterArgs& a0, const Tuning& tu, hipStream_t s) {
   const int64_t waves = (int64_t)a.T * a.ngrp + a.pad.nwaves;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb)), block(wpb * kWave);
   if (tu.nontemporal >= 1)
-    hipLaunchKernelGGL((scatter_kernel<DT, CPL, SCALE, true>), grid, block, 0, s, a);
+    launch_kernel(scatter_kernel<DT, CPL, SCALE, true>, grid, block, 0, s, tu, a);
   else
-    hipLaunchKernelGGL((scatter_kernel<DT, CPL, SCALE, false>), grid, block, 0, s, a);
+    launch_kernel(scatter_kernel<DT, CPL, SCALE, false>, grid, block, 0, s, tu, a);
   return hipGetLastError();
 }
 
@@ -324,9 +324,9 @@ hipError_t go_gather(const GatherArgs& a0, const Tuning& tu, hipStream_t s) {
   const int64_t waves = (int64_t)a.T * a.ngrp;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb)), block(wpb * kWave);
   switch (tu.nontemporal) {
-    case 0: hipLaunchKernelGGL((gather_kernel<DT, CPL, W, false, false>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((gather_kernel<DT, CPL, W, true, false>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((gather_kernel<DT, CPL, W, true, true>), grid, block, 0, s, a); break;
+    case 0: launch_kernel(gather_kernel<DT, CPL, W, false, false>, grid, block, 0, s, tu, a); break;
+    case 1: launch_kernel(gather_kernel<DT, CPL, W, true, false>, grid, block, 0, s, tu, a); break;
+    default: launch_kernel(gather_kernel<DT, CPL, W, true, true>, grid, block, 0, s, tu, a); break;
   }
   return hipGetLastError();
 }
@@ -352,9 +352,9 @@ hipError_t go_dot(const DotArgs& a, const Tuning& tu, hipStream_t s) {
   const size_t lds = (size_t)nseg * a.K * sizeof(float);
   const dim3 grid((unsigned)a.T), block(nw * kWave);
   switch (tu.nontemporal) {
-    case 0: hipLaunchKernelGGL((token_dot_kernel<DT, G, W, false, false>), grid, block, lds, s, a); break;
-    case 1: hipLaunchKernelGGL((token_dot_kernel<DT, G, W, true, false>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((token_dot_kernel<DT, G, W, true, true>), grid, block, lds, s, a); break;
+    case 0: launch_kernel(token_dot_kernel<DT, G, W, false, false>, grid, block, lds, s, tu, a); break;
+    case 1: launch_kernel(token_dot_kernel<DT, G, W, true, false>, grid, block, lds, s, tu, a); break;
+    default: launch_kernel(token_dot_kernel<DT, G, W, true, true>, grid, block, lds, s, tu, a); break;
   }
   return hipGetLastError();
 }

@@ -258,9 +258,9 @@ hipError_t go_send(StagedArgs a, const Tuning& tu, hipStream_t s) {
   a.ngrp = segments(a.NV);
   const dim3 grid = grid_for(a.T, a.ngrp, tu.waves_per_block), block(tu.waves_per_block * kWave);
   if (tu.nontemporal >= 1)
-    hipLaunchKernelGGL((send_kernel<DT, true>), grid, block, 0, s, a);
+    launch_kernel(send_kernel<DT, true>, grid, block, 0, s, tu, a);
   else
-    hipLaunchKernelGGL((send_kernel<DT, false>), grid, block, 0, s, a);
+    launch_kernel(send_kernel<DT, false>, grid, block, 0, s, tu, a);
   return hipGetLastError();
 }
 
@@ -271,11 +271,11 @@ hipError_t go_expand(StagedArgs a, const Tuning& tu, hipStream_t s) {
              block(tu.waves_per_block * kWave);
   const bool nt = tu.nontemporal >= 1;
   if (a.scale) {
-    if (nt) hipLaunchKernelGGL((expand_kernel<DT, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((expand_kernel<DT, true, false>), grid, block, 0, s, a);
+    if (nt) launch_kernel(expand_kernel<DT, true, true>, grid, block, 0, s, tu, a);
+    else launch_kernel(expand_kernel<DT, true, false>, grid, block, 0, s, tu, a);
   } else {
-    if (nt) hipLaunchKernelGGL((expand_kernel<DT, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((expand_kernel<DT, false, false>), grid, block, 0, s, a);
+    if (nt) launch_kernel(expand_kernel<DT, false, true>, grid, block, 0, s, tu, a);
+    else launch_kernel(expand_kernel<DT, false, false>, grid, block, 0, s, tu, a);
   }
   return hipGetLastError();
 }
@@ -286,11 +286,11 @@ hipError_t go_reduce(StagedArgs a, const Tuning& tu, hipStream_t s) {
   const dim3 grid = grid_for(a.send_cap, a.ngrp, tu.waves_per_block), block(tu.waves_per_block * kWave);
   const bool nt = tu.nontemporal >= 1;
   if (a.w) {
-    if (nt) hipLaunchKernelGGL((reduce_partitions_kernel<DT, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((reduce_partitions_kernel<DT, true, false>), grid, block, 0, s, a);
+    if (nt) launch_kernel(reduce_partitions_kernel<DT, true, true>, grid, block, 0, s, tu, a);
+    else launch_kernel(reduce_partitions_kernel<DT, true, false>, grid, block, 0, s, tu, a);
   } else {
-    if (nt) hipLaunchKernelGGL((reduce_partitions_kernel<DT, false, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((reduce_partitions_kernel<DT, false, false>), grid, block, 0, s, a);
+    if (nt) launch_kernel(reduce_partitions_kernel<DT, false, true>, grid, block, 0, s, tu, a);
+    else launch_kernel(reduce_partitions_kernel<DT, false, false>, grid, block, 0, s, tu, a);
   }
   return hipGetLastError();
 }
@@ -300,9 +300,9 @@ hipError_t go_combine_partitions(StagedArgs a, const Tuning& tu, hipStream_t s) 
   a.ngrp = segments(a.NV);
   const dim3 grid = grid_for(a.T, a.ngrp, tu.waves_per_block), block(tu.waves_per_block * kWave);
   if (tu.nontemporal >= 1)
-    hipLaunchKernelGGL((combine_partitions_kernel<DT, true>), grid, block, 0, s, a);
+    launch_kernel(combine_partitions_kernel<DT, true>, grid, block, 0, s, tu, a);
   else
-    hipLaunchKernelGGL((combine_partitions_kernel<DT, false>), grid, block, 0, s, a);
+    launch_kernel(combine_partitions_kernel<DT, false>, grid, block, 0, s, tu, a);
   return hipGetLastError();
 }
 

@@ -315,6 +315,21 @@ int moe_stream_destroy(hipStream_t stream);
  * byte count.  Not part of the method.                                    */
 int moe_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
+/* Measurement hook (not part of the method).  The next kernel that a row
+ * call on this handle launches (moe_dispatch, moe_combine, moe_combine_bwd,
+ * moe_dispatch_bwd or a staged call; the first kernel of a call that has
+ * two) is launched with hipExtLaunchKernel: stop is bound to that kernel's
+ * completion, and start, when not NULL, is recorded just before it, so
+ * that their elapsed time is the kernel's own execution, without the launch
+ * latency that events recorded around the call include.  A stop alone costs
+ * nothing measurable (consecutive stops give exact periods); a start adds a
+ * marker to the stream (about 3 us of GPU time on MI355X).  One-shot: the
+ * launch consumes them.  Both NULL disarms.  The events belong to the
+ * caller, were created on the call's device, and must stay alive until the
+ * call's stream has passed them.  Returns MOE_ERR_INVALID_ARG for a bad
+ * handle, or a start without a stop. */
+int moe_time_next_kernel(moe_handle_t h, hipEvent_t start, hipEvent_t stop);
+
 /* Message for a status code (static string). */
 const char* moe_strerror(int status);
 

@@ -136,6 +136,19 @@ def test_row_calls_need_a_layout(L, handle):
     assert L.moe_handle_check(handle, None, ctypes.byref(st)) == C["MOE_ERR_HANDLE"]
 
 
+def test_time_next_kernel_validation(L, handle):
+    """The measurement hook only stores the events; a row call that fails
+    validation launches nothing, so the hook stays armed for the next one."""
+    ev = ctypes.c_void_p(FAKE)
+    assert L.moe_time_next_kernel(None, ev, ev) == C["MOE_ERR_INVALID_ARG"]
+    assert L.moe_time_next_kernel(handle, ev, None) == C["MOE_ERR_INVALID_ARG"]
+    assert L.moe_time_next_kernel(handle, None, ev) == C["MOE_OK"]   # a stop alone
+    assert L.moe_time_next_kernel(handle, ev, ev) == C["MOE_OK"]
+    p = ctypes.c_void_p(FAKE)
+    assert L.moe_combine(handle, p, 1, 2048, None, p, None) == C["MOE_ERR_HANDLE"]
+    assert L.moe_time_next_kernel(handle, None, None) == C["MOE_OK"]  # disarmed
+
+
 def test_copy_validation(L):
     p = ctypes.c_void_p(FAKE)
     assert L.moe_bench_copy(p, p, 15, None) == C["MOE_ERR_SHAPE"]

@@ -57,12 +57,21 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
+    """The counters stay valid while the dominant kernel, its launcher and
+    the device helpers are unchanged; an edit elsewhere in the file keeps
+    them, an edit to the kernel drops them."""
     cfg = W.get_config("qwen3_30b_a3b")
     (tmp_path / "profiles").mkdir()
     csrc = tmp_path / "combine_moe_layout_04_amd" / "csrc"
     csrc.mkdir(parents=True)
-    for f in ("row_kernels.hip", "staged_kernels.hip", "device_common.h"):
-        (csrc / f).write_text(f"// {f}\n")
+
+    def source(kernel, launcher, body="  a.x = 1;", other="// other code"):
+        return (f"{other}\ntemplate <int DT>\n__global__ __launch_bounds__(512) void {kernel}(Args a) {{\n{body}\n}}\n"
+                f"\ntemplate <int DT>\nhipError_t {launcher}(Args a) {{\n  return 0;\n}}\n")
+
+    (csrc / "row_kernels.hip").write_text(source("gather_kernel", "go_gather"))
+    (csrc / "staged_kernels.hip").write_text(source("reduce_partitions_kernel", "go_reduce"))
+    (csrc / "device_common.h").write_text("// helpers\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     hd, hs = bench.kernel_source_hash(False), bench.kernel_source_hash(True)
     (tmp_path / "profiles" / f"traffic_{cfg.name}.md").write_text(
@@ -70,6 +79,10 @@ def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
         f"source_hash.combine:reduce: {hs}\ntraffic_bytes_per_launch.combine:reduce: 456\n")
     assert bench.traffic_from_profiles(cfg) == 123
     assert bench.traffic_from_profiles(cfg, True) == 456
-    (csrc / "staged_kernels.hip").write_text("// changed\n")
+    (csrc / "row_kernels.hip").write_text(source("gather_kernel", "go_gather", other="// edited elsewhere"))
+    assert bench.traffic_from_profiles(cfg) == 123
+    (csrc / "staged_kernels.hip").write_text(source("reduce_partitions_kernel", "go_reduce", body="  a.x = 2;"))
     assert bench.traffic_from_profiles(cfg) == 123
     assert bench.traffic_from_profiles(cfg, True) is None
+    (csrc / "device_common.h").write_text("// helpers, changed\n")
+    assert bench.traffic_from_profiles(cfg) is None
