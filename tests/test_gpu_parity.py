@@ -248,6 +248,22 @@ def test_k_above_one_group(absorbed, dtype, H):
     compare_layer(cfg, res, ref)
 
 
+@pytest.mark.parametrize("absorbed", [False, True])
+@pytest.mark.parametrize("dtype,H,T", [("bf16", 520, 1000), ("f32", 260, 333)])
+def test_maximum_k_experts_and_partitions(absorbed, dtype, H, T):
+    # the ABI's limits at once: K = 32 (four groups of eight rows per token,
+    # 16-token layout tiles), E = 1024 experts, P = 64 partitions
+    base = W.get_config("qwen3_30b_a3b")
+    cfg = base.with_(T=T, H=H, dtype=dtype, E=1024, P=64, K=32, absorbed=absorbed,
+                     renormalize=not absorbed)
+    say(f"K=32 E=1024 P=64 T={T} {dtype} H={H} absorbed={absorbed}")
+    inp = W.layer_inputs(cfg, seed=31)
+    h, res = run_layer(cfg, inp)
+    _, ref = oracle_layer(cfg, inp)
+    compare_layer(cfg, res, ref)
+    check_layout(h, O.layout(inp.topk_idx, cfg.E, cfg.P))
+
+
 def test_unscaled_dispatch_with_scores_and_both_backward_modes():
     cfg = W.get_config("qwen3_30b_a3b", T=300)
     inp = W.layer_inputs(cfg, seed=4)
