@@ -48,8 +48,21 @@ def _run(cmd):
     return r.stdout
 
 
+C_ABI_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "moe_c_abi_check.cpp")
+C_ABI_CHECK = os.path.join(ROOT, "tests", "c_abi", "moe_c_abi_check")
+
+
+def build_c_abi_check() -> str:
+    """The C++ program that drives the library through its C ABI alone (no
+    Python, no torch), linked against the in-tree library; returns its path."""
+    _run([hipcc(), f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-I", INCLUDE, C_ABI_CHECK_SRC,
+          "-o", C_ABI_CHECK, "-L", PKG, "-lmoe_layout", "-Wl,-rpath,$ORIGIN/../../combine_moe_layout_04_amd"])
+    return C_ABI_CHECK
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
+    """Compile every HIP source and link the shared library (then the C ABI
+    check program against it); returns the library's path."""
     cc = hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
@@ -63,6 +76,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     outs.append(_run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))
     os.replace(tmp, LIB)
+    build_c_abi_check()
     if verbose:
         for o in outs:
             if o.strip():
