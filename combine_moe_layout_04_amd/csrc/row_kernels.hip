@@ -1,5 +1,5 @@
 // Row movement between token order [T,H] and the expert-grouped receive
-// buffer [R,H], R = T*K.
+// buffer [R,H], R = T*K (plus the padding rows of a padded handle).
 //
 // A row is cut into 16-byte chunks and the chunks into segments of 64: one
 // wavefront-wide access is one segment, 1 KiB of one row, fully coalesced.
@@ -12,6 +12,8 @@
 //     and stores it to the K receive rows, optionally scaled by w[t,k] in
 //     float32 and rounded (scores absorbed before W2).  The receive rows are
 //     written once and not read back here, so their stores are non-temporal.
+//     On a padded handle, waves after the token waves zero the padding rows
+//     (pad_fill.h).
 //   gather (receive rows -> token): forward combine, and the backward of an
 //     unscaled dispatch.  One wave loads its segment of up to 8 receive rows
 //     at once (non-temporal: read once), sums them in float32 in k order from
