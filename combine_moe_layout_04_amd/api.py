@@ -93,12 +93,15 @@ def moe_workspace_size(T: int, K: int, E: int, P: int, pad_multiple: int = 1) ->
 
 
 _SIZES = {}  # (T, K, E, P, pad_multiple) -> workspace bytes (pure host functions of the shape)
+_SIZES_MAX = 4096  # a job with many distinct token counts starts the cache over past this
 
 
 def _workspace_bytes(T, K, E, P, pad):
     key = (T, K, E, P, pad)
     v = _SIZES.get(key)
     if v is None:
+        if len(_SIZES) >= _SIZES_MAX:
+            _SIZES.clear()
         v = _SIZES[key] = moe_workspace_size(T, K, E, P, pad)
     return v
 
