@@ -809,9 +809,11 @@ def main():
             "bytes_per_step": step_b,
             "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
             "us_per_step": round(ms_per_step * 1e3, 2),
-            "call_avg_us": {n: round(v, 2) for n, v in avg_us.items()},
-            "call_median_us": {n: round(v, 2) for n, v in med_us.items()},
-            "call_GBps": {n: round(row_bytes[n] / (avg_us[n] * 1e-6) / 1e9, 1) for n in avg_us if row_bytes[n]},
+            **({} if not avg_us else {  # --events all: per-call intervals, records included
+                "call_avg_us": {n: round(v, 2) for n, v in avg_us.items()},
+                "call_median_us": {n: round(v, 2) for n, v in med_us.items()},
+                "call_GBps": {n: round(row_bytes[n] / (avg_us[n] * 1e-6) / 1e9, 1) for n in avg_us if row_bytes[n]},
+            }),
             "index_bytes_per_step": index_bytes(cfg, args.staged, n_send, pad_rows),
             **({} if m == 1 else {"pad_multiple": m, "padding_rows": pad_rows}),
             "host_enqueue_us_per_step": round(host_us, 1),
