@@ -326,9 +326,9 @@ int moe_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream)
  * marker to the stream (about 3 us of GPU time on MI355X).  One-shot: the
  * launch consumes them.  Both NULL disarms.  The events belong to the
  * caller, were created on the call's device, and must stay alive until the
- * call's stream has passed them.  Not for a stream under graph capture (the
- * launch then fails with MOE_ERR_HIP).  Returns MOE_ERR_INVALID_ARG for a bad
- * handle, or a start without a stop. */
+ * call's stream has passed them.  Meant for eager launches: its use under
+ * graph capture is untested.  Returns MOE_ERR_INVALID_ARG for a bad handle,
+ * or a start without a stop. */
 int moe_time_next_kernel(moe_handle_t h, hipEvent_t start, hipEvent_t stop);
 
 /* Message for a status code (static string). */
