@@ -264,6 +264,20 @@ def test_maximum_k_experts_and_partitions(absorbed, dtype, H, T):
     check_layout(h, O.layout(inp.topk_idx, cfg.E, cfg.P))
 
 
+@pytest.mark.parametrize("absorbed", [False, True])
+def test_long_context_token_count(absorbed):
+    # a long-context batch: 131072 tokens (over a million (t,k) pairs, 2048
+    # tokens per layout tile), narrow rows so the oracle stays quick
+    base = W.get_config("qwen3_30b_a3b")
+    cfg = base.with_(T=131072, H=64, absorbed=absorbed, renormalize=not absorbed)
+    say(f"long context T={cfg.T} H={cfg.H} absorbed={absorbed}")
+    inp = W.layer_inputs(cfg, seed=51)
+    h, res = run_layer(cfg, inp)
+    _, ref = oracle_layer(cfg, inp)
+    compare_layer(cfg, res, ref)
+    check_layout(h, O.layout(inp.topk_idx, cfg.E, cfg.P))
+
+
 def test_unscaled_dispatch_with_scores_and_both_backward_modes():
     cfg = W.get_config("qwen3_30b_a3b", T=300)
     inp = W.layer_inputs(cfg, seed=4)
