@@ -223,6 +223,19 @@ def kernel_source_hash(staged=False):
     return h.hexdigest()[:16]
 
 
+def sources_hash():
+    """Hash of every library source and the public header: which code a result
+    line measured (the repository's history does not travel with the tree)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_moe_layout_04_amd", "csrc")
+    paths = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    for path in paths + [os.path.join(ROOT, "include", "moe_layout.h")]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def traffic_from_profiles(cfg, staged=False):
     """HBM bytes per launch of the dominant call's kernel from the committed
     counter summary (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known
@@ -836,6 +849,7 @@ def main():
             }),
             "tuning": {"chunks_per_lane": args.chunks_per_lane, "nontemporal": args.nontemporal,
                        "waves_per_block": args.waves_per_block, "layout_pairs": args.layout_pairs},
+            "sources_sha256": sources_hash(),
         },
         "roofline": None if achieved is None else {
             "bound": "hbm",

@@ -86,3 +86,19 @@ def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
     assert bench.traffic_from_profiles(cfg, True) is None
     (csrc / "device_common.h").write_text("// helpers, changed\n")
     assert bench.traffic_from_profiles(cfg) is None
+
+
+def test_sources_hash_names_the_code(tmp_path, monkeypatch):
+    """The result line's sources hash changes with any library source."""
+    csrc = tmp_path / "combine_moe_layout_04_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "include").mkdir()
+    (tmp_path / "include" / "moe_layout.h").write_text("// header\n")
+    (csrc / "a.hip").write_text("// a\n")
+    (csrc / "notes.txt").write_text("not a source\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.sources_hash()
+    (csrc / "notes.txt").write_text("changed, still not a source\n")
+    assert bench.sources_hash() == h0
+    (csrc / "a.hip").write_text("// a, changed\n")
+    assert bench.sources_hash() != h0
