@@ -84,14 +84,15 @@ __global__ __launch_bounds__(512) void send_kernel(StagedArgs a) {
   const int t = gw / a.ngrp;
   if (t >= a.T) return;  // wave-uniform
   const int j = (gw - t * a.ngrp) * kWave + lane;
-  int row;
-  unsigned long long m = token_rows(a, t, row);
-  const bool bad = lane < a.P && ((m >> lane) & 1ull) && (unsigned)row >= (unsigned)a.send_cap;
-  if (j - lane == 0) flag_bad(a.status, bad);
+  // the token row's segment first: its load does not wait for the send rows
   const u32x4* src = static_cast<const u32x4*>(a.src) + (size_t)t * a.NV;
   u32x4* dst = static_cast<u32x4*>(a.dst);
   u32x4 v = {0u, 0u, 0u, 0u};  // defined on every lane: see expand_kernel
   if (j < a.NV) v = src[j];
+  int row;
+  unsigned long long m = token_rows(a, t, row);
+  const bool bad = lane < a.P && ((m >> lane) & 1ull) && (unsigned)row >= (unsigned)a.send_cap;
+  if (j - lane == 0) flag_bad(a.status, bad);
   while (m) {  // uniform
     const int r = __builtin_ctzll(m);
     m &= m - 1;
