@@ -114,19 +114,22 @@ __global__ __launch_bounds__(512) void expand_kernel(StagedArgs a) {
   const int s = gw / a.ngrp;
   if (s >= a.send_cap) return;  // wave-uniform
   const int grp = gw - s * a.ngrp;
-  int t, pos;
-  float w;
-  uint64_t km;
-  if (!send_row_pairs(a, s, t, km, pos, w)) return;  // uniform
-  if (grp == 0 && a.scores_out && ((km >> lane) & 1ull)) a.scores_out[pos] = w;
+  if (s >= a.send_offset[a.P]) return;  // uniform: a send row past N_send holds nothing
   const int j = grp * kWave + lane;
   const u32x4* src = static_cast<const u32x4*>(a.src);
   u32x4* dst = static_cast<u32x4*>(a.dst);
+  // The send row's segment first: its load needs only the row, so it
+  // overlaps the round trips that find the row's token and pairs.
   // v must hold a defined value on the lanes past the row end as well: the
   // scaled path converts it on every lane, and a conversion of an
   // indeterminate value lets the compiler drop the j < NV guards.
   u32x4 v = {0u, 0u, 0u, 0u};
   if (j < a.NV) v = load_chunk<NT>(src + (size_t)s * a.NV + j);
+  int t, pos;
+  float w;
+  uint64_t km;
+  if (!send_row_pairs(a, s, t, km, pos, w)) return;  // uniform
+  if (grp == 0 && a.scores_out && ((km >> lane) & 1ull)) a.scores_out[pos] = w;
   float f[SCALE ? V : 1];
   if constexpr (SCALE) unpack<DT>(v, f);
   while (km) {  // uniform
