@@ -204,6 +204,10 @@ __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a) {
 template <int DT, bool GATHER, bool WEIGHTED, bool NTL, bool NTS>
 __global__ __launch_bounds__(1024) void token_dot_kernel(DotArgs a) {
   constexpr int V = Elems<DT>::kPerChunk;
+  // Rows in flight per group.  The bfloat16 gather variant keeps a sum and
+  // the token segment unpacked beside its rows: with 8 rows it needs 79
+  // VGPRs (6 waves per SIMD), with 4 it fits 64 (8 waves per SIMD).
+  constexpr int KGD = (GATHER && DT == kBF16) ? 4 : KG;
   extern __shared__ float seg_val[];  // [nseg][K]
   const int lane = lane_id();
   const int wave = (int)(threadIdx.x / kWave);
@@ -220,22 +224,26 @@ __global__ __launch_bounds__(1024) void token_dot_kernel(DotArgs a) {
   for (int sg = wave; sg < nseg; sg += nw) {  // wave-uniform
     const int j = sg * kWave + lane;
     const bool valid = j < a.NV;
+    u32x4 xr = u32x4{0u, 0u, 0u, 0u};
+    if (valid) xr = tok[j];
     float x[V];
-    if (valid) {
-      unpack<DT>(tok[j], x);
-    } else {
 #pragma unroll
-      for (int i = 0; i < V; ++i) x[i] = 0.f;
-    }
+    for (int i = 0; i < V; ++i) x[i] = 0.f;
+    // The gather variant unpacks the token segment only after its first
+    // group of receive-row loads has gone out, so both loads share one round
+    // trip.  The row-free dot unpacks it first: its rows then go out after
+    // the token's, which measured faster at the 14-segment row width.
+    constexpr bool kLate = GATHER;
+    if constexpr (!kLate) unpack<DT>(xr, x);
     float acc[GATHER ? V : 1];
 #pragma unroll
     for (int i = 0; i < (GATHER ? V : 1); ++i) acc[i] = 0.f;
 
-    for (int kg = 0; kg < a.K; kg += KG) {
-      u32x4 yv[KG];
-      bool ok[KG];
+    for (int kg = 0; kg < a.K; kg += KGD) {
+      u32x4 yv[KGD];
+      bool ok[KGD];
 #pragma unroll
-      for (int kk = 0; kk < KG; ++kk) {
+      for (int kk = 0; kk < KGD; ++kk) {
         const int k = kg + kk;
         ok[kk] = false;
         yv[kk] = u32x4{0u, 0u, 0u, 0u};
@@ -245,8 +253,11 @@ __global__ __launch_bounds__(1024) void token_dot_kernel(DotArgs a) {
           if (ok[kk] && valid) yv[kk] = load_chunk<NTL>(rcv + (size_t)p * a.NV + j);
         }
       }
+      if constexpr (kLate) {
+        if (kg == 0) unpack<DT>(xr, x);
+      }
 #pragma unroll
-      for (int kk = 0; kk < KG; ++kk) {
+      for (int kk = 0; kk < KGD; ++kk) {
         const int k = kg + kk;
         if (k < a.K) {  // uniform: every lane takes part in the fold
           float c = 0.f;

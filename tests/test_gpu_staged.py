@@ -115,6 +115,7 @@ RAGGED = [("tiny", dict(T=37)), ("tiny", dict(T=129, H=12)), ("qwen3_30b_a3b", d
 
 @pytest.mark.parametrize("name,over", RAGGED)
 @pytest.mark.parametrize("tuning", [dict(), dict(nontemporal=0, waves_per_block=1),
+                                    dict(nontemporal=1, waves_per_block=2),
                                     dict(nontemporal=2, waves_per_block=8)])
 def test_staged_ragged(name, over, tuning):
     cfg = W.get_config(name, **over)
