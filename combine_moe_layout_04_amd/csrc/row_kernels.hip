@@ -16,8 +16,10 @@
 //     (pad_fill.h).
 //   gather (receive rows -> token): forward combine, and the backward of an
 //     unscaled dispatch.  One wave loads its segment of up to 8 receive rows
-//     at once (non-temporal: read once), sums them in float32 in k order from
-//     +0.0 (product and sum rounded separately) and rounds once.
+//     (non-temporal: read once), sums them in float32 in k order from +0.0
+//     (product and sum rounded separately) and rounds once.  The compiled
+//     code issues the 8 loads one after another; issuing them together
+//     measured no faster, since the resident waves already keep HBM busy.
 //   token dot (one workgroup per token, one wave per segment): the
 //     router-weight gradients <tok[t], rcv[recv_pos[t,k]]>, in the fixed
 //     order of moe_layout.h: per-chunk partials in element order, a butterfly
@@ -35,7 +37,7 @@
 namespace moe {
 namespace {
 
-constexpr int KG = 8;  // receive rows in flight together per wave
+constexpr int KG = 8;  // receive rows per group of loads
 
 template <bool NT>
 __device__ __forceinline__ u32x4 load_chunk(const u32x4* p) {
