@@ -1,10 +1,13 @@
 """Negative controls on the GPU side: the planted mistakes of the oracle
 mutants (tests/test_oracle_mutants.py: score faults, dropped or unscaled
 gradients, misaligned rows, wrong intra-expert order, off-by-one offsets,
-other dot orders, truncating bf16 rounding) must each make the GPU-vs-oracle
-comparison fail, while the real oracle matches the GPU bit for bit.  The
-mistakes live in the oracle, on the CPU; the GPU runs the real kernels once.
-The comparison's bar is zero ulp, so it is below the smallest fault."""
+other dot orders, truncating bf16 rounding; tests/test_oracle_staged.py:
+shifted send rows, the wrong partition in the expansion, a partition reduce
+that ignores partitions, descending partition order in the merge) must each
+make the GPU-vs-oracle comparison fail, while the real oracle matches the GPU
+bit for bit.  The mistakes live in the oracle, on the CPU; the GPU runs the
+real kernels once.  The comparison's bar is zero ulp, so it is below the
+smallest fault."""
 import numpy as np
 import pytest
 import torch
@@ -14,6 +17,7 @@ import combine_moe_layout_04_amd as M
 from oracle import moe_oracle as O
 
 import test_oracle_mutants as MU
+import test_oracle_staged as MS
 from devutil import n_diff, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -127,3 +131,52 @@ def test_scaled_backward_forgetting_the_scale(absorbed):
     m_gx, _ = MU.dispatch_bwd_forgets_scale(lay, inp.grad_recv, cfg.dtype, w, inp.x)
     assert n_diff(res["gs"], r_gs) == 0
     differs(res["gx"], r_gx, m_gx, "dispatch_bwd without the scale")
+
+
+@pytest.fixture(scope="module")
+def staged():
+    """One staged exchange (send, expansion, partition reduce, merge) on the
+    GPU, float32 rows so that the merge's summation order shows in its bits."""
+    cfg = W.get_config("qwen3_30b_a3b", T=512).with_(dtype="f32")
+    inp = W.layer_inputs(cfg, seed=43)
+    say(f"negative controls, staged: T={cfg.T} H={cfg.H} {cfg.dtype} P={cfg.P}")
+    dt = cfg.dtype
+    idx = torch.from_numpy(inp.topk_idx).to(DEV)
+    w = torch.from_numpy(inp.topk_weights).to(DEV)
+    x, y = to_dev(inp.x, dt, DEV), to_dev(inp.y, dt, DEV)
+    h = M.moe_layout(idx, cfg.E, cfg.P)
+    n = int(h.field("send_offset")[-1].item())
+    S = M.moe_send(h, x)
+    recv, _ = M.moe_expand(h, S, w)
+    Q = M.moe_reduce_partitions(h, y, w)
+    out = M.moe_combine_partitions(h, Q)
+    assert h.check() == 0
+    res = dict(S=to_host(S[:n], dt), recv=to_host(recv, dt), Q=to_host(Q[:n], dt), out=to_host(out, dt))
+    return cfg, inp, O.layout(inp.topk_idx, cfg.E, cfg.P), res
+
+
+def test_staged_send_shifted_rows(staged):
+    cfg, inp, lay, res = staged
+    differs(res["S"], O.send(lay, inp.x), MS.send_off_by_one(lay, inp.x), "send")
+
+
+def test_staged_expand_wrong_partition(staged):
+    cfg, inp, lay, res = staged
+    S = O.send(lay, inp.x)
+    w = inp.topk_weights
+    differs(res["recv"], O.expand(lay, S, cfg.dtype, w)[0], MS.expand_wrong_partition(lay, S, cfg.dtype, w)[0],
+            "expand")
+
+
+def test_staged_reduce_ignoring_partitions(staged):
+    cfg, inp, lay, res = staged
+    w = inp.topk_weights
+    differs(res["Q"], O.reduce_partitions(lay, inp.y, cfg.dtype, w),
+            MS.reduce_ignores_partition(lay, inp.y, cfg.dtype, w), "reduce_partitions")
+
+
+def test_staged_merge_descending_order(staged):
+    cfg, inp, lay, res = staged
+    Q = O.reduce_partitions(lay, inp.y, cfg.dtype, inp.topk_weights)
+    differs(res["out"], O.combine_partitions(lay, Q, cfg.dtype), MS.combine_partitions_descending(lay, Q, cfg.dtype),
+            "combine_partitions")
