@@ -3,7 +3,9 @@ mutants (tests/test_oracle_mutants.py: score faults, dropped or unscaled
 gradients, misaligned rows, wrong intra-expert order, off-by-one offsets,
 other dot orders, truncating bf16 rounding; tests/test_oracle_staged.py:
 shifted send rows, the wrong partition in the expansion, a partition reduce
-that ignores partitions, descending partition order in the merge) must each
+that ignores partitions, descending partition order in the merge;
+tests/test_oracle_padding.py: segments rounded down, padding placed first,
+stale padding rows) must each
 make the GPU-vs-oracle comparison fail, while the real oracle matches the GPU
 bit for bit.  The mistakes live in the oracle, on the CPU; the GPU runs the
 real kernels once.  The comparison's bar is zero ulp, so it is below the
@@ -17,6 +19,7 @@ import combine_moe_layout_04_amd as M
 from oracle import moe_oracle as O
 
 import test_oracle_mutants as MU
+import test_oracle_padding as MP
 import test_oracle_staged as MS
 from devutil import n_diff, to_dev, to_host
 
@@ -180,3 +183,47 @@ def test_staged_merge_descending_order(staged):
     Q = O.reduce_partitions(lay, inp.y, cfg.dtype, inp.topk_weights)
     differs(res["out"], O.combine_partitions(lay, Q, cfg.dtype), MS.combine_partitions_descending(lay, Q, cfg.dtype),
             "combine_partitions")
+
+
+PAD_M = 16
+
+
+@pytest.fixture(scope="module")
+def padded():
+    """A layout padded to multiples of 16 and its dispatch on the GPU; the
+    receive buffer starts full of NaN so that padding rows left unwritten
+    would show."""
+    cfg = W.get_config("qwen3_30b_a3b", T=512)
+    inp = W.layer_inputs(cfg, seed=44)
+    say(f"negative controls, padded m={PAD_M}: T={cfg.T} H={cfg.H} {cfg.dtype}")
+    dt = cfg.dtype
+    idx = torch.from_numpy(inp.topk_idx).to(DEV)
+    w = torch.from_numpy(inp.topk_weights).to(DEV)
+    h = M.moe_layout(idx, cfg.E, cfg.P, handle=M.Handle(pad_multiple=PAD_M))
+    recv = torch.full((h.R, cfg.H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    recv, sc = M.moe_dispatch(h, to_dev(inp.x, dt, DEV), w, recv=recv, recv_scores=True)
+    assert h.check() == 0
+    fields = {f: h.field(f).cpu().numpy() for f in ("expert_offset", "recv_pos", "recv_token", "recv_k")}
+    lay = O.layout(inp.topk_idx, cfg.E, cfg.P, PAD_M)
+    end = int(lay.expert_offset[-1])
+    return cfg, inp, lay, dict(recv=to_host(recv, dt)[:end], sc=sc.cpu().numpy()[:end], end=end, **fields)
+
+
+@pytest.mark.parametrize("mutant", [MP.layout_floor, MP.layout_pad_at_front])
+def test_padded_layout_faults(padded, mutant):
+    cfg, inp, lay, res = padded
+    bad = mutant(inp.topk_idx, cfg.E, cfg.P, PAD_M)
+    names = ("expert_offset", "recv_pos", "recv_token", "recv_k")
+    for f in names:
+        assert np.array_equal(res[f], np.asarray(getattr(lay, f))), f
+    assert any(not np.array_equal(res[f], np.asarray(getattr(bad, f))) for f in names), mutant.__name__
+
+
+def test_padded_dispatch_stale_padding(padded):
+    cfg, inp, lay, res = padded
+    w = inp.topk_weights
+    r_recv, r_sc = O.dispatch(lay, inp.x, cfg.dtype, w)
+    m_recv, _ = MP.dispatch_no_zero_fill(lay, inp.x, cfg.dtype, w)
+    end = res["end"]
+    assert n_diff(res["sc"], r_sc[:end]) == 0
+    differs(res["recv"], r_recv[:end], m_recv[:end], "padded dispatch")
