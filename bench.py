@@ -14,10 +14,15 @@ HBM-bound and is measured against the HBM roofline.
   checkpointing; the combine is never replayed) and run the combine backward
   (a copy) and the scaled dispatch backward (rows + score gradient).
 
-Cold HBM: every kernel of a step reads buffers that were last touched more
-than 1 GB of traffic earlier (several rotating buffer sets, and the combine
-backward reads its own copy of the expert output), so the 256 MB Infinity
-Cache cannot serve them.  ``--warm`` chains the real tensors instead
+Cold HBM: the step rotates over buffer sets that together span at least
+12 GiB (``--sets`` overrides the count), and the combine backward reads its
+own copy of the expert output, so the 256 MB Infinity Cache cannot serve a
+buffer from one use to the next.  A shallow rotation is not enough: the
+token rows are read with ordinary loads, while the receive rows move with
+non-temporal accesses that leave the cache alone, so three sets of the
+Qwen3-30B-A3B shape (33 MB of token rows each) kept the token rows resident.
+That step measured 140.4 us with 3 sets, 146.8 with 8, 150.0 with 16 and
+150.2-150.6 with 24 to 48.  ``--warm`` chains the real tensors instead
 (combine reads what dispatch wrote) as a secondary figure.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 is not supported (the path is
@@ -38,6 +43,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
+COLD_SPAN_BYTES = 12 << 30  # the rotating buffer sets span at least this much
+MAX_SETS = 64
 METRIC = "dispatch+combine fwd+bwd GB/s per layer and % of MI355X HBM peak"
 
 
@@ -47,7 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="qwen3_30b_a3b")
-    ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets (cold HBM)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating buffer sets (cold HBM); 0: enough to span COLD_SPAN_BYTES, at least 3")
     ap.add_argument("--warm", action="store_true", help="chain tensors: combine reads dispatch's output")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -536,10 +544,15 @@ def main():
     def empty_rows(n):
         return torch.empty((n, cfg.H), dtype=tdt, device=dev)
 
-    nsets = 1 if args.warm else max(1, args.sets)
     ws_bytes = M.moe_workspace_size(cfg.T, cfg.K, cfg.E, cfg.P, m)
     sets = []
-    for _ in range(nsets):
+
+    def set_bytes(s):
+        n = sum(t.numel() * t.element_size() for k, t in s.items() if torch.is_tensor(t))
+        return n + sum(t.numel() * t.element_size() for q in s["pass"] for t in q.values() if torch.is_tensor(t))
+
+    nsets = 1 if args.warm else max(1, args.sets)
+    while len(sets) < nsets:
         s = {"pass": [], "y": y0.clone(), "g": g0.clone()}
         if not args.warm:
             s["y_bwd"] = y0.clone()      # the backward's own copy of the expert output
@@ -556,6 +569,8 @@ def main():
         s["grad_w"] = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device=dev)
         s["grad_x"] = empty_rows(cfg.T)
         sets.append(s)
+        if not args.warm and args.sets <= 0 and len(sets) == 1:
+            nsets = min(MAX_SETS, max(3, -(-COLD_SPAN_BYTES // max(1, set_bytes(s)))))
     del y0, g0, gr0, per_pass
 
     # padding rows of each pass's routing (the same in every buffer set)
@@ -666,7 +681,7 @@ def main():
     assert d != ncall - 1, "the step's last call carries the step-boundary event"
     for i in range(args.warmup):
         step(sets[i % nsets])
-    for s in sets:
+    for s in sets[:min(nsets, args.warmup)]:  # the sets the warmup ran
         for q in s["pass"]:
             assert q["h"].check() == 0
 
@@ -818,7 +833,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: T={cfg.T} H={cfg.H} {dt} E={cfg.E} P={cfg.P} K={cfg.K}, {protocol}",
-            "cache": "warm (chained tensors)" if args.warm else f"cold ({nsets} rotating buffer sets)",
+            "cache": ("warm (chained tensors)" if args.warm else
+                      f"cold ({nsets} rotating buffer sets, {nsets * set_bytes(sets[0]) / 1e9:.1f} GB)"),
             "bytes_per_step": step_b,
             "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
             "us_per_step": round(ms_per_step * 1e3, 2),

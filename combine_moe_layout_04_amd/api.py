@@ -146,6 +146,8 @@ class Handle:
 
     def check(self) -> int:
         """Synchronises the current stream and returns the device status bits."""
+        if self.device is None:
+            raise RuntimeError("moe_handle_check: the handle has no layout yet")
         v = ctypes.c_int(0)
         _check(lib().moe_handle_check(self._h, _stream(self.device), ctypes.byref(v)), "moe_handle_check")
         return v.value

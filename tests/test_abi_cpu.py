@@ -200,3 +200,12 @@ def test_cu_budget_stream_validation(L):
     assert L.moe_stream_create_cu_budget(-1, 8, ctypes.byref(s)) == C["MOE_ERR_INVALID_ARG"]
     assert L.moe_stream_create_cu_budget(0, 0, ctypes.byref(s)) == C["MOE_ERR_INVALID_ARG"]
     assert L.moe_stream_destroy(None) == C["MOE_ERR_INVALID_ARG"]
+
+
+def test_python_handle_check_needs_a_layout(L):
+    """The binding refuses a device check on a handle that has run no layout
+    (it has no device yet), with a clear error and no HIP call."""
+    import combine_moe_layout_04_amd as M
+    h = M.Handle()
+    with pytest.raises(RuntimeError, match="no layout yet"):
+        h.check()
