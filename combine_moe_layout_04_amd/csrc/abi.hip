@@ -357,10 +357,12 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   a.scale = topk_weights != nullptr;
   a.status = ws_ptr<int>(h, h->plan.status);
   a.pad = pad_rows(h, grad_y, nullptr, NV);  // no gradient in the padding rows
-  st = grad_y ? hip_status(moe::launch_scatter(a, take_tuning(h), stream)) : MOE_OK;
-  if (st != MOE_OK || !grad_w) return st;
-  // router-weight gradient: a separate pass over grad_out and y (measured
-  // faster than fusing it into the row stores: HBM turns around less)
+  if (!grad_w) return hip_status(moe::launch_scatter(a, take_tuning(h), stream));
+  // Router-weight gradient: a separate pass over grad_out and y (measured
+  // faster than fusing it into the row stores: HBM turns around less).  It
+  // goes first: the two passes are independent, and the read-only pass ahead
+  // of the row scatter measured level at the Qwen3-30B-A3B shape and 3 us
+  // faster per layer at the DeepSeek-V3 shape.
   moe::DotArgs d{};
   d.tok = grad_out;
   d.rcv = y;
@@ -374,7 +376,9 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
   d.dtype = dtype;
   d.gather = false;
   d.status = a.status;
-  return hip_status(moe::launch_token_dot(d, take_tuning(h), stream));
+  st = hip_status(moe::launch_token_dot(d, take_tuning(h), stream));
+  if (st != MOE_OK || !grad_y) return st;
+  return hip_status(moe::launch_scatter(a, take_tuning(h), stream));
 }
 
 int moe_dispatch_bwd(moe_handle_t h, const void* grad_recv, int dtype, int64_t H,

@@ -83,23 +83,25 @@ __global__ __launch_bounds__(512) void scatter_kernel(ScatterArgs a) {
   const int grp = gw - t * a.ngrp;
   const int jb = grp * kWave * CPL + lane;  // this lane's first chunk
 
-  const Pairs q = load_pairs(a.recv_pos, a.w, t, a.K, a.R);
-  if (grp == 0) {
-    if (__ballot(q.bad) && lane == 0) atomicOr(a.status, MOE_STATUS_BAD_POSITION);
-    if (a.scores_out && lane < a.K && !q.bad) a.scores_out[q.pos] = q.w;
-  }
-
-  const u32x4* src = static_cast<const u32x4*>(a.src) + (size_t)t * a.NV;
-  u32x4* dst = static_cast<u32x4*>(a.dst);
+  // The token row's segment first: its load needs only t, so it shares a
+  // round trip with the pair lookups instead of following them.
   // Lanes past the row end hold zeros: the scaled path converts every lane's
   // chunk, and a conversion of an indeterminate value would let the
   // compiler drop the j < NV guards.
+  const u32x4* src = static_cast<const u32x4*>(a.src) + (size_t)t * a.NV;
+  u32x4* dst = static_cast<u32x4*>(a.dst);
   u32x4 v[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int j = jb + c * kWave;
     v[c] = u32x4{0u, 0u, 0u, 0u};
     if (j < a.NV) v[c] = src[j];
+  }
+
+  const Pairs q = load_pairs(a.recv_pos, a.w, t, a.K, a.R);
+  if (grp == 0) {
+    if (__ballot(q.bad) && lane == 0) atomicOr(a.status, MOE_STATUS_BAD_POSITION);
+    if (a.scores_out && lane < a.K && !q.bad) a.scores_out[q.pos] = q.w;
   }
   float f[CPL][SCALE ? V : 1];
   if constexpr (SCALE) {
