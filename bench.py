@@ -193,18 +193,26 @@ def index_bytes(cfg, staged=False, n_send=None, pad_rows=None):
 
 # The call whose kernel the roofline reports: the K-row gather-reduce (in the
 # staged exchange, its receiver-side half).
-DOMINANT = {False: "combine", True: "combine:reduce"}
+# The call whose kernel is the step's longest launch, measured cold: the
+# dispatch's row scatter on every direct shape (Qwen3-30B-A3B 29.0 us against
+# 27.3 for the combine's gather; DeepSeek-V3 110.0 against 97.2; the
+# DiffusionGemma scaled dispatch 78.6 us, five times a step), and on the
+# staged path the dispatch's expansion (39.5 us, beside the combine
+# backward's scaled expansion at 40.6 and the partition reduce at 37.4).
+DOMINANT = {False: "dispatch", True: "dispatch:expand"}
+DOMINANT_KERNEL = {False: "scatter_kernel: token row to its K receive rows",
+                   True: "expand_kernel: send row to its pairs' receive rows"}
 # what the committed traffic counters describe: the dominant kernel's
-# function, its launcher, and the device helpers it uses
-KERNEL_SOURCES = {False: ("row_kernels.hip", ("gather_kernel", "go_gather")),
-                  True: ("staged_kernels.hip", ("reduce_partitions_kernel", "go_reduce"))}
+# function, its launcher, and the device headers it uses
+KERNEL_SOURCES = {False: ("row_kernels.hip", ("scatter_kernel", "go_scatter"), ("device_common.h", "pad_fill.h")),
+                  True: ("staged_kernels.hip", ("expand_kernel", "go_expand"), ("device_common.h", "pad_fill.h"))}
 
 
 def dominant_call(cfg, staged=False):
     name = DOMINANT[staged]
     if not cfg.absorbed:
         return name
-    return name.replace("combine", "combine.0", 1)
+    return name.replace("dispatch", "dispatch.0", 1)
 
 
 def function_text(src, name):
@@ -219,15 +227,16 @@ def function_text(src, name):
 
 def kernel_source_hash(staged=False):
     """Hash of the dominant kernel's source (the counters' subject): its
-    function, its launcher and device_common.h."""
+    function, its launcher and the device headers it uses."""
     csrc = os.path.join(ROOT, "combine_moe_layout_04_amd", "csrc")
-    path, funcs = KERNEL_SOURCES[staged]
+    path, funcs, headers = KERNEL_SOURCES[staged]
     src = open(os.path.join(csrc, path)).read()
     h = hashlib.sha256()
     for f in funcs:
         h.update(function_text(src, f).encode())
-    with open(os.path.join(csrc, "device_common.h"), "rb") as fh:
-        h.update(fh.read())
+    for name in headers:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -869,8 +878,7 @@ def main():
         },
         "roofline": None if achieved is None else {
             "bound": "hbm",
-            "kernel": f"{dom} (" + ("reduce_partitions_kernel: per-partition K-row gather-reduce)"
-                                    if args.staged else "gather_kernel: K-row gather-reduce)"),
+            "kernel": f"{dom} ({DOMINANT_KERNEL[args.staged]})",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

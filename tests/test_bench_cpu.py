@@ -42,7 +42,8 @@ def test_staged_absorbed_step_has_three_passes_and_two_backwards():
     names = [c[0] for c in calls]
     assert names.count("layout.0") == 1 and "replay_layout.2" in names and "replay_layout.1" not in names
     assert sum(1 for c in calls if c[1] == "dot_s") == 2
-    assert bench.dominant_call(cfg, True) == "combine.0:reduce"
+    assert bench.dominant_call(cfg, True) == "dispatch.0:expand"
+    assert bench.dominant_call(cfg) == "dispatch.0"
     NS = {p: n * cfg.H * cfg.esize for p, n in enumerate([10, 20, 30])}
     for name, kind, p, b in calls:
         if kind.startswith("send"):
@@ -69,22 +70,23 @@ def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
         return (f"{other}\ntemplate <int DT>\n__global__ __launch_bounds__(512) void {kernel}(Args a) {{\n{body}\n}}\n"
                 f"\ntemplate <int DT>\nhipError_t {launcher}(Args a) {{\n  return 0;\n}}\n")
 
-    (csrc / "row_kernels.hip").write_text(source("gather_kernel", "go_gather"))
-    (csrc / "staged_kernels.hip").write_text(source("reduce_partitions_kernel", "go_reduce"))
+    (csrc / "row_kernels.hip").write_text(source("scatter_kernel", "go_scatter"))
+    (csrc / "staged_kernels.hip").write_text(source("expand_kernel", "go_expand"))
     (csrc / "device_common.h").write_text("// helpers\n")
+    (csrc / "pad_fill.h").write_text("// padding waves\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     hd, hs = bench.kernel_source_hash(False), bench.kernel_source_hash(True)
     (tmp_path / "profiles" / f"traffic_{cfg.name}.md").write_text(
-        f"source_hash.combine: {hd}\ntraffic_bytes_per_launch.combine: 123\n"
-        f"source_hash.combine:reduce: {hs}\ntraffic_bytes_per_launch.combine:reduce: 456\n")
+        f"source_hash.dispatch: {hd}\ntraffic_bytes_per_launch.dispatch: 123\n"
+        f"source_hash.dispatch:expand: {hs}\ntraffic_bytes_per_launch.dispatch:expand: 456\n")
     assert bench.traffic_from_profiles(cfg) == 123
     assert bench.traffic_from_profiles(cfg, True) == 456
-    (csrc / "row_kernels.hip").write_text(source("gather_kernel", "go_gather", other="// edited elsewhere"))
+    (csrc / "row_kernels.hip").write_text(source("scatter_kernel", "go_scatter", other="// edited elsewhere"))
     assert bench.traffic_from_profiles(cfg) == 123
-    (csrc / "staged_kernels.hip").write_text(source("reduce_partitions_kernel", "go_reduce", body="  a.x = 2;"))
+    (csrc / "staged_kernels.hip").write_text(source("expand_kernel", "go_expand", body="  a.x = 2;"))
     assert bench.traffic_from_profiles(cfg) == 123
     assert bench.traffic_from_profiles(cfg, True) is None
-    (csrc / "device_common.h").write_text("// helpers, changed\n")
+    (csrc / "pad_fill.h").write_text("// padding waves, changed\n")
     assert bench.traffic_from_profiles(cfg) is None
 
 
