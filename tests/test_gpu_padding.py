@@ -123,7 +123,7 @@ def run_and_check(cfg, inp, m, tuning=None):
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen3_30b_a3b", "deepseek_v3", "diffusion_gemma",
-                                  "skewed_literal"])
+                                  "skewed_literal", "skewed_calibrated"])
 @pytest.mark.parametrize("m", [16, 128])
 def test_padded_full_size(name, m):
     cfg = W.get_config(name)

@@ -207,6 +207,87 @@ def test_layer_full_size(name):
     compare_layer(cfg, res, ref)
 
 
+U32 = 2.0 ** -24   # unit roundoff of float32
+U64 = 2.0 ** -53
+
+
+def gamma(n, u):
+    return n * u / (1 - n * u)
+
+
+def dot_depth(H, dtype):
+    """Most roundings any one product undergoes in the library's float32 dot
+    of two length-H rows: its own rounding, at most V adds inside its
+    16-byte chunk (V elements per chunk, the first add to +0.0 counted), six
+    adds of the 64-lane fold, and one add per 64-chunk segment."""
+    V = 4 if dtype == "f32" else 8
+    nseg = -(-(H // V) // 64)
+    return 1 + V + 6 + nseg
+
+
+def exact_dots(a, b, dtype, pos, chunk=256):
+    """For every pair (t, k): the fp64 dot <tok[t], rcv[pos[t,k]]> and the
+    sum of |products|, where `a` holds the token rows [T,H] and `b` the
+    receive rows [R,H] (products of bf16 or float32 inputs are exact in
+    fp64)."""
+    T, K = pos.shape
+    d = np.empty((T, K))
+    m = np.empty((T, K))
+    for t0 in range(0, T, chunk):
+        A = as_f64(a[t0:t0 + chunk], dtype)
+        B = as_f64(b[pos[t0:t0 + chunk].reshape(-1)], dtype).reshape(A.shape[0], K, -1)
+        d[t0:t0 + chunk] = np.einsum("nh,nkh->nk", A, B)
+        m[t0:t0 + chunk] = np.einsum("nh,nkh->nk", np.abs(A), np.abs(B))
+    return d, m
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_router_gradients_against_their_definition(name):
+    """grad_w (weighted layers) and grad_s (scores absorbed) from the GPU,
+    element by element, against the exact dot that defines them, within
+    the error bound of float32 summation that holds for ANY order in which
+    no product sees more than D roundings (Higham, "Accuracy and Stability
+    of Numerical Algorithms", 2nd ed., section 3.1: |fl(x.y) - x.y| <=
+    gamma_D * sum|x_i y_i|).  This does not depend on the library's own
+    summation tree, which the bit-exact oracle comparison pins separately.
+    A dropped, doubled or misaligned score is an O(1) error here: the same
+    check against a neighbouring k, or against twice the value, must fail
+    almost everywhere."""
+    cfg = W.get_config(name)
+    say(f"router gradients {name} T={cfg.T} H={cfg.H} {cfg.dtype} K={cfg.K}")
+    inp = W.layer_inputs(cfg, seed=7)
+    _, res = run_layer(cfg, inp)
+    assert res["status"] == 0
+    pos = O.layout(inp.topk_idx, cfg.E, cfg.P).recv_pos
+    if cfg.absorbed:   # grad_s[t,k] = <grad_recv[recv_pos[t,k]], x[t]>
+        got = res["grad_s"]
+        exact, mag = exact_dots(inp.x, inp.grad_recv, cfg.dtype, pos)
+    else:              # grad_w[t,k] = <g[t], y[recv_pos[t,k]]>
+        got = res["grad_w"]
+        exact, mag = exact_dots(inp.g, inp.y, cfg.dtype, pos)
+    bound = (gamma(dot_depth(cfg.H, cfg.dtype), U32) + gamma(cfg.H, U64)) * mag
+    err = np.abs(got.astype(np.float64) - exact)
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    say(f"  max |err| / bound = {worst:.3e} (max |err| {err.max():.3e}, max |dot| {np.abs(exact).max():.2f})")
+    assert np.all(err <= bound), f"{int(np.sum(err > bound))} router gradients outside the bound"
+    # negative controls: the bound tells right from wrong
+    rolled = np.abs(np.roll(got, 1, axis=1).astype(np.float64) - exact) > bound
+    doubled = np.abs(2.0 * got.astype(np.float64) - exact) > bound
+    assert rolled.mean() > 0.99 and doubled.mean() > 0.99, (rolled.mean(), doubled.mean())
+
+
+def test_layer_full_size_int64_ids():
+    """A whole layer (every call) on int64 expert ids, at full size."""
+    cfg = W.get_config("qwen3_30b_a3b")
+    say(f"layer int64 ids T={cfg.T} H={cfg.H} E={cfg.E} P={cfg.P} K={cfg.K}")
+    inp = W.layer_inputs(cfg, seed=12, idx_dtype=np.int64)
+    assert inp.topk_idx.dtype == np.int64
+    h, res = run_layer(cfg, inp)
+    lay, ref = oracle_layer(cfg, inp)
+    check_layout(h, lay)
+    compare_layer(cfg, res, ref)
+
+
 RAGGED = [  # name, overrides
     ("tiny", dict(T=37)),
     ("tiny", dict(T=129, H=12)),
@@ -223,7 +304,9 @@ RAGGED = [  # name, overrides
                                     dict(chunks_per_lane=2, nontemporal=2, waves_per_block=8,
                                          layout_pairs=2048),
                                     dict(chunks_per_lane=4, nontemporal=1, waves_per_block=2,
-                                         layout_pairs=4096)])
+                                         layout_pairs=4096),
+                                    dict(gather_mode=1),
+                                    dict(gather_mode=1, nontemporal=0, waves_per_block=8)])
 def test_layer_ragged_rows_all_tunings(name, over, tuning):
     cfg = W.get_config(name, **over)
     say(f"ragged {name} {over} {tuning}")
@@ -231,6 +314,32 @@ def test_layer_ragged_rows_all_tunings(name, over, tuning):
     h, res = run_layer(cfg, inp, tuning=tuning)
     _, ref = oracle_layer(cfg, inp)
     compare_layer(cfg, res, ref)
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_lds_staged_gather_full_size(name):
+    """The LDS-staged gather (receive rows loaded straight into LDS) gives the
+    register gather's sums bit for bit, on every full-size layer, for the
+    combine (weighted or plain) and the unscaled dispatch backward; the
+    combine is also checked against the oracle."""
+    cfg = W.get_config(name)
+    dt = cfg.dtype
+    say(f"lds gather {name} T={cfg.T} H={cfg.H} {dt} K={cfg.K}")
+    inp = W.layer_inputs(cfg, seed=8)
+    idx = torch.from_numpy(inp.topk_idx).to(DEV)
+    w = None if cfg.absorbed else torch.from_numpy(inp.topk_weights).to(DEV)
+    y, gr = (to_dev(a, dt, DEV) for a in (inp.y, inp.grad_recv))
+    outs = {}
+    for mode in (0, 1):
+        h = M.moe_layout(idx, cfg.E, cfg.P, handle=M.Handle(gather_mode=mode))
+        outs[mode] = (M.moe_combine(h, y, w), M.moe_dispatch_bwd(h, gr)[0])
+        assert h.check() == 0
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16 if dt == "bf16" else torch.int32),
+                           b.view(torch.int16 if dt == "bf16" else torch.int32))
+    lay = O.layout(inp.topk_idx, cfg.E, cfg.P)
+    ref = O.combine(lay, inp.y, dt, None if cfg.absorbed else inp.topk_weights)
+    assert np.array_equal(to_host(outs[1][0], dt), ref)
 
 
 @pytest.mark.parametrize("absorbed", [False, True])
@@ -427,6 +536,33 @@ def test_autograd_wrappers(absorbed):
     assert np.array_equal(to_host(x.grad, dt), r_gx)
     assert w.grad is not None                     # the router keeps learning
     assert np.array_equal(w.grad.cpu().numpy(), r_gs if absorbed else r_gw)
+
+
+def test_autograd_refuses_a_handle_laid_out_again():
+    """A per-layer handle reused by a later forward pass before the first
+    pass's backward: the backward must raise, not use the newer routing."""
+    from combine_moe_layout_04_amd import autograd as A
+    cfg = W.get_config("tiny")
+    dt = cfg.dtype
+    inp = W.layer_inputs(cfg, seed=13)
+    inp2 = W.layer_inputs(cfg, seed=14)
+    w = torch.from_numpy(inp.topk_weights).to(DEV).requires_grad_(True)
+    x = to_dev(inp.x, dt).requires_grad_(True)
+    h = M.moe_layout(torch.from_numpy(inp.topk_idx).to(DEV), cfg.E, cfg.P)
+    recv, _ = A.dispatch(x, None, h)
+    out = A.combine(recv * 1.0, w, h)
+    M.moe_layout(torch.from_numpy(inp2.topk_idx).to(DEV), cfg.E, cfg.P, handle=h)  # re-layout
+    with pytest.raises(A.StaleLayoutError):
+        out.backward(to_dev(inp.g, dt))
+    # the same graph with the layout replayed first runs, and matches the oracle
+    M.moe_layout(torch.from_numpy(inp.topk_idx).to(DEV), cfg.E, cfg.P, handle=h)
+    x2 = to_dev(inp.x, dt).requires_grad_(True)
+    recv2, _ = A.dispatch(x2, None, h)
+    A.combine(recv2 * 1.0, w, h).backward(to_dev(inp.g, dt))
+    lay = O.layout(inp.topk_idx, cfg.E, cfg.P)
+    r_recv, _ = O.dispatch(lay, inp.x, dt)
+    r_gy, _ = O.combine_bwd(lay, inp.g, dt, inp.topk_weights, r_recv)
+    assert np.array_equal(to_host(x2.grad, dt), O.dispatch_bwd(lay, r_gy, dt)[0])
 
 
 # ----------------------------------------------------------- ABI on device --

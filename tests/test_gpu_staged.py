@@ -98,8 +98,8 @@ def compare(cfg, res, ref):
         assert n_diff(res["dot"], ref["dot"]) == 0
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen3_30b_a3b", "skewed_literal", "deepseek_v3",
-                                  "diffusion_gemma"])
+@pytest.mark.parametrize("name", ["tiny", "qwen3_30b_a3b", "skewed_literal", "skewed_calibrated",
+                                  "deepseek_v3", "diffusion_gemma"])
 @pytest.mark.parametrize("part", ["fwd", "bwd"])
 def test_staged_full_size(name, part):
     cfg = W.get_config(name)
