@@ -110,8 +110,8 @@ class Handle:
     """Opaque layout handle plus the device workspace its arrays live in."""
 
     def __init__(self, chunks_per_lane: int = 0, nontemporal: int = 2, waves_per_block: int = 0,
-                 layout_pairs: int = 0, pad_multiple: int = 1):
-        tun = MoeTuning(chunks_per_lane, nontemporal, waves_per_block, layout_pairs)
+                 layout_pairs: int = 0, pad_multiple: int = 1, gather_mode: int = 0):
+        tun = MoeTuning(chunks_per_lane, nontemporal, waves_per_block, layout_pairs, gather_mode)
         h = ctypes.c_void_p()
         _check(lib().moe_handle_create_padded(ctypes.byref(h), ctypes.byref(tun), int(pad_multiple)),
                "moe_handle_create")
@@ -120,6 +120,10 @@ class Handle:
         self.workspace: Optional[torch.Tensor] = None
         self.T = self.K = self.E = self.P = self.R = None
         self.device = None
+        # Layouts computed on this handle so far.  The C handle only ever
+        # holds its latest layout, so a backward pass checks that the layout
+        # its forward used is still the one in place.
+        self.generation = 0
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -184,6 +188,7 @@ def moe_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
         _check(lib().moe_recv_capacity(h.ptr, ctypes.byref(n)), "moe_recv_capacity")
         h.R = n.value  # receive rows: T*K, plus the padding capacity of a padded handle
     h.workspace, h.T, h.K, h.E, h.P, h.device = ws, T, K, E, P, dev
+    h.generation += 1
     return h
 
 

@@ -1,11 +1,16 @@
 """Autograd wrappers: one handle shared by a Dispatch and its paired Combine.
 
-The backward of a combine is a dispatch and the backward of a dispatch is a
-combine, both replayed against the forward dispatch's handle ("Add an opt-in
-DeepEP transport for the AutoEP expert all-to-all", section "Why").  Both
-backward passes return the router-weight gradient: returning None for it
-silently stops the gate from learning, the bug that page's review fix
-describes.  Nothing here computes: every step is a library call.
+Each backward pass runs the opposite row movement on the routing the forward
+used: the dispatch's backward sums receive-row gradients back to tokens, and
+the combine's backward spreads the output gradient to the receive rows
+("Add an opt-in DeepEP transport for the AutoEP expert all-to-all", section
+"Why").  Both return the router-weight gradient, without which the gate
+would stop learning (the review fix on that page).  Nothing here computes:
+every step is a library call.
+
+The C handle keeps only its latest layout.  A backward pass whose handle was
+laid out again after its forward (for example a per-layer handle reused by a
+later forward pass) raises instead of using the newer routing.
 """
 from __future__ import annotations
 
@@ -16,12 +21,25 @@ import torch
 from . import api
 
 
+class StaleLayoutError(RuntimeError):
+    """The handle was laid out again between a forward pass and its backward."""
+
+
+def _same_layout(ctx, what):
+    if ctx.handle.generation != ctx.generation:
+        raise StaleLayoutError(
+            f"{what} backward: the handle holds layout {ctx.handle.generation}, but the forward pass "
+            f"used layout {ctx.generation}; give each forward pass that takes a backward its own handle, "
+            "or replay the layout before the backward")
+
+
 class _Dispatch(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, topk_weights, handle, scale_rows):
         recv, scores = api.moe_dispatch(handle, x, topk_weights, scale_rows=scale_rows,
                                         recv_scores=topk_weights is not None)
         ctx.handle = handle
+        ctx.generation = handle.generation
         ctx.scale_rows = bool(scale_rows)
         ctx.save_for_backward(x if scale_rows else None, topk_weights if scale_rows else None)
         if scores is not None:
@@ -33,6 +51,7 @@ class _Dispatch(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_recv, _grad_scores):
+        _same_layout(ctx, "dispatch")
         x, w = ctx.saved_tensors
         want_s = ctx.scale_rows and ctx.needs_input_grad[1]
         grad_x, grad_s = api.moe_dispatch_bwd(ctx.handle, grad_recv.contiguous(),
@@ -46,12 +65,14 @@ class _Combine(torch.autograd.Function):
     def forward(ctx, y, topk_weights, handle):
         out = api.moe_combine(handle, y, topk_weights)
         ctx.handle = handle
+        ctx.generation = handle.generation
         ctx.weighted = topk_weights is not None
         ctx.save_for_backward(y if ctx.weighted else None, topk_weights)
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
+        _same_layout(ctx, "combine")
         y, w = ctx.saved_tensors
         want_w = ctx.weighted and ctx.needs_input_grad[1]
         grad_y, grad_w = api.moe_combine_bwd(ctx.handle, grad_out.contiguous(), w,
