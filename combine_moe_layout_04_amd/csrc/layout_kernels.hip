@@ -89,12 +89,21 @@ __global__ __launch_bounds__(kLT) void layout_count_kernel(LayoutArgs a) {
   }
   __syncthreads();
 
-  for (int tt = tid; tt < nt; tt += kLT) {
-    unsigned long long m = msk[tt];
-    while (m) {
-      const int r = __ffsll(m) - 1;
-      m &= m - 1;
-      atomicAdd(&rh[r], 1);
+  if (nt <= kWave) {  // uniform: lane = token; one ballot per partition, spread over the waves
+    const int lane = tid & (kWave - 1);
+    const unsigned long long m = lane < nt ? msk[lane] : 0ull;
+    for (int r = tid / kWave; r < a.P; r += kLW) {
+      const int c = __popcll(__ballot((int)((m >> r) & 1ull)));
+      if (lane == 0) rh[r] = c;
+    }
+  } else {
+    for (int tt = tid; tt < nt; tt += kLT) {
+      unsigned long long m = msk[tt];
+      while (m) {
+        const int r = __ffsll(m) - 1;
+        m &= m - 1;
+        atomicAdd(&rh[r], 1);
+      }
     }
   }
   __syncthreads();  // before any global store (a barrier would wait for them)
@@ -141,23 +150,11 @@ __device__ __forceinline__ void column_sums(const int* __restrict__ h, int NR, i
   }
 }
 
-// Start of every histogram column, globally and at tile b.  The histogram is
-// tile-major, h[j * NR + r]: count of column r (a bucket, then a partition)
-// in tile j.  Writes col_n[r] = column r's total, col_0[r] = sum of all
-// columns before r (col_0[NR] = the total) and col_b[r] = col_0[r] + column
-// r's count in the tiles before b.  The first npad columns (the experts)
-// take pad * ceil(total / pad) rows in the running sum: padded segments.
-// Each thread sums a range of tiles of one column with all its loads in
-// flight (clamped, unconditional loads); a workgroup scan over the column
-// totals follows.  part: LDS [2][parts][NR].  Ends with a barrier.
-__device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int b, int npad, int pad,
-                               int* col_b, int* col_0, int* col_n, int* part, int* wsum) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
-  const int parts = max(1, min(nblk, kLT / NR));  // threads per column
-  const int cpp = (nblk + parts - 1) / parts;     // tiles per thread
-  // loads in flight per thread: the tiles it sums, rounded up a short ladder
+// column_sums with a batch of loads sized to the tiles each thread sums,
+// rounded up a short ladder.
+__device__ __forceinline__ void all_column_sums(const int* __restrict__ h, int NR, int nblk, int b, int parts,
+                                                int* part) {
+  const int cpp = (nblk + parts - 1) / parts;  // tiles per thread
   if (cpp <= 4)
     column_sums<4>(h, NR, nblk, b, parts, cpp, part);
   else if (cpp <= 8)
@@ -174,6 +171,24 @@ __device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int 
     column_sums<48>(h, NR, nblk, b, parts, cpp, part);
   else
     column_sums<kColRegs>(h, NR, nblk, b, parts, cpp, part);
+}
+
+// Start of every histogram column, globally and at tile b.  The histogram is
+// tile-major, h[j * NR + r]: count of column r (a bucket, then a partition)
+// in tile j.  Writes col_n[r] = column r's total, col_0[r] = sum of all
+// columns before r (col_0[NR] = the total) and col_b[r] = col_0[r] + column
+// r's count in the tiles before b.  The first npad columns (the experts)
+// take pad * ceil(total / pad) rows in the running sum: padded segments.
+// Each thread sums a range of tiles of one column with all its loads in
+// flight (clamped, unconditional loads); a workgroup scan over the column
+// totals follows.  part: LDS [2][parts][NR].  Ends with a barrier.
+__device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int b, int npad, int pad,
+                               int* col_b, int* col_0, int* col_n, int* part, int* wsum) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int parts = max(1, min(nblk, kLT / NR));  // threads per column
+  all_column_sums(h, NR, nblk, b, parts, part);
   __syncthreads();
   int carry = 0;
   for (int c0 = 0; c0 < NR; c0 += kLT) {  // uniform
@@ -463,6 +478,187 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   }
 }
 
+// ---- rank, one round of 64 pairs per wave --------------------------------------
+//
+// The usual case: a tile of at most kLT pairs (one per thread, so wave w holds
+// pairs [64w, 64w+64) of the tile) and at most kLT histogram columns.  The
+// results equal layout_rank_kernel's, with three workgroup barriers instead of
+// about seven: what depends on the tile alone (each pair's rank among the equal
+// ids of its wave, the wave's bucket counts, the tile's token masks, the token
+// ballots) is done before or beside the scan, and the scan's last step also
+// turns the wave counts into each (wave, bucket)'s first receive row.
+
+__global__ __launch_bounds__(kLT) void layout_rank_wave_kernel(LayoutArgs a) {
+  extern __shared__ __align__(8) unsigned char smem[];
+  const int E1 = a.E + 1;
+  const int NR = E1 + a.P;  // histogram columns, at most kLT here
+  const int parts = max(1, min(a.nblk, kLT / NR));
+  const int ngmax = (a.tile + kWave - 1) / kWave;  // token groups of 64 in a tile
+  unsigned long long* colm = reinterpret_cast<unsigned long long*>(smem);  // [ngmax][P] group g's tokens in r
+  unsigned long long* tm = colm + ngmax * a.P;   // [tile] the tile's token masks
+  int* base = reinterpret_cast<int*>(tm + a.tile);  // [NR]   this tile's start of each column
+  int* off = base + NR;                          // [NR+1] start of each column, tile 0
+  int* coln = off + NR + 1;                      // [NR]   column totals (unpadded)
+  int* cnt = coln + NR;                          // [kLW][E+1] wave bucket counts, then first rows
+  int* wsum = cnt + kLW * E1;                    // [kLW]
+  int* part = wsum + kLW;                        // [2][parts][NR] column partial sums
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int t0 = b * a.tile;
+  const int nt = max(0, min(a.T, t0 + a.tile) - t0);
+  const int np = nt * a.K;
+  const int64_t p0 = (int64_t)t0 * a.K;
+
+  // 0. this thread's pair and token mask: their round trips overlap the
+  //    histogram's.  Threads without a pair take an id no pair has.
+  const int e = tid < np ? load_expert(a.idx, a.itype, p0 + tid, a.E) : a.E + 1;
+  const unsigned long long mk = tid < nt ? a.tok_mask[t0 + tid] : 0ull;
+  int* mycnt = cnt + wv * E1;
+  for (int j = lane; j < E1; j += kWave) mycnt[j] = 0;
+
+  // 1. column sums of the histogram, all of a thread's loads in flight
+  all_column_sums(a.hist, NR, a.nblk, b, parts, part);
+
+  // 2. rank among the equal ids of this wave (wave64 ballots over the id
+  //    bits), and the wave's count of each bucket, written by the highest
+  //    lane of each group of equal ids
+  const int nbits = 32 - __clz(a.E + 1);  // enough bits for ids 0..E+1
+  uint64_t same = ~0ull;
+  for (int bit = 0; bit < nbits; ++bit) {
+    const int on = (e >> bit) & 1;
+    const uint64_t bb = __ballot(on);
+    same &= on ? bb : ~bb;
+  }
+  const int rank = __popcll(same & lanes_below(lane));
+  __builtin_amdgcn_wave_barrier();  // the wave's row is cleared before its counts land
+  if (tid < np && (same >> lane) == 1ull) mycnt[e] = __popcll(same);
+  if (tid < nt) tm[tid] = mk;
+  __syncthreads();  // (1)
+
+  // 3. the scan's first half: each column's total, its count in the tiles
+  //    before this one, and the rows it takes (padded for the experts); a
+  //    wave scan over the columns.  Beside it, one ballot per (token group,
+  //    partition) over the tile's token masks, spread over the waves.
+  int tot = 0, pre = 0;
+  if (tid < NR) {
+    for (int q = 0; q < parts; ++q) {
+      tot += part[q * NR + tid];
+      pre += part[(parts + q) * NR + tid];
+    }
+  }
+  const int seg = (tid < a.E) ? (tot + a.pad - 1) / a.pad * a.pad : tot;  // rows the column takes
+  const int inc = wave_inclusive_scan(seg);
+  if (lane == kWave - 1) wsum[wv] = inc;
+  const int ng = (nt + kWave - 1) / kWave;
+  for (int j = wv; j < ng * a.P; j += kLW) {  // uniform per wave
+    const int g = j / a.P;
+    const int r = j - g * a.P;
+    const int t = g * kWave + lane;
+    const unsigned long long m = t < nt ? tm[t] : 0ull;
+    const uint64_t bal = __ballot((int)((m >> r) & 1ull));
+    if (lane == 0) colm[j] = bal;
+  }
+  __syncthreads();  // (2)
+
+  // 4. every column's start, globally (off) and at this tile (base); for the
+  //    buckets, each (wave, bucket)'s first receive row: the tile's start
+  //    plus the wave counts of the tile's earlier waves
+  if (tid < NR) {
+    int st = inc - seg;
+#pragma unroll
+    for (int w = 0; w < kLW; ++w) {
+      const int ws = wsum[w];
+      if (w < wv) st += ws;
+    }
+    off[tid] = st;
+    base[tid] = st + pre;
+    coln[tid] = tot;
+    if (tid == NR - 1) off[NR] = st + seg;
+    if (tid < E1) {
+      int run = st + pre;
+#pragma unroll
+      for (int w = 0; w < kLW; ++w) {
+        const int c = cnt[w * E1 + tid];
+        cnt[w * E1 + tid] = run;
+        run += c;
+      }
+    }
+  }
+  __syncthreads();  // (3): global stores only from here on
+
+  // 5. stable receive positions
+  const int R = a.R;
+  if (tid < np) {
+    const int pos = cnt[wv * E1 + e] + rank;
+    if ((unsigned)pos < (unsigned)R) {
+      const int tq = tid / a.K;
+      a.recv_pos[p0 + tid] = pos;
+      a.recv_token[pos] = t0 + tq;
+      a.recv_k[pos] = tid - tq * a.K;
+    } else {
+      atomicOr(a.status, MOE_STATUS_BAD_POSITION);
+    }
+  }
+
+  // 6. token send slots and their inverse
+  if (nt <= kWave) {  // uniform: one token group, the unrolled store rounds
+    switch ((nt * a.P + kLT - 1) / kLT) {
+      case 0: break;
+      case 1: write_slots<1>(a, colm, base, off, t0, nt); break;
+      case 2: write_slots<2>(a, colm, base, off, t0, nt); break;
+      case 3: write_slots<3>(a, colm, base, off, t0, nt); break;
+      case 4: write_slots<4>(a, colm, base, off, t0, nt); break;
+      case 5: write_slots<5>(a, colm, base, off, t0, nt); break;
+      case 6: write_slots<6>(a, colm, base, off, t0, nt); break;
+      case 7: write_slots<7>(a, colm, base, off, t0, nt); break;
+      default: write_slots<kSlotRounds>(a, colm, base, off, t0, nt); break;
+    }
+  } else {  // several groups of 64 tokens: a token's slot adds the earlier groups' counts
+    for (int i = tid; i < nt * a.P; i += kLT) {
+      const int tt = i / a.P;
+      const int r = i - tt * a.P;
+      const int g = tt / kWave;
+      const int l = tt - g * kWave;
+      int before = 0;
+      for (int gg = 0; gg < g; ++gg) before += __popcll(colm[gg * a.P + r]);
+      const uint64_t bal = colm[g * a.P + r];
+      const int slot = base[E1 + r] - off[E1 + r] + before + __popcll(bal & lanes_below(l));
+      const bool on = (bal >> l) & 1ull;
+      a.token_slot[(size_t)t0 * a.P + i] = on ? slot : -1;
+      if (on) a.send_token[off[E1 + r] - off[E1] + slot] = t0 + tt;
+    }
+  }
+
+  // 7. padded layouts: receive rows that hold no pair get -1 in the inverse maps
+  if (a.pad > 1) {  // uniform
+    for (int x = b; x < a.E; x += a.nblk) {
+      const int hi = min(off[x + 1], R);
+      for (int p = off[x] + coln[x] + tid; p < hi; p += kLT) {
+        a.recv_token[p] = -1;
+        a.recv_k[p] = -1;
+      }
+    }
+    for (int p = off[E1] + b * kLT + tid; p < R; p += a.nblk * kLT) {
+      a.recv_token[p] = -1;
+      a.recv_k[p] = -1;
+    }
+  }
+
+  // 8. global counts, offsets and status (tile 0 writes them)
+  if (b == 0) {
+    const int total = off[E1];  // the bucket columns come first
+    for (int x = tid; x < a.E; x += kLT) a.num_tokens_per_expert[x] = coln[x];
+    for (int x = tid; x <= a.E; x += kLT) a.expert_offset[x] = off[x];
+    for (int r = tid; r <= a.P; r += kLT) a.rank_offset[r] = off[r * a.epr];
+    for (int r = tid; r < a.P; r += kLT) a.num_tokens_per_rank[r] = off[E1 + r + 1] - off[E1 + r];
+    for (int r = tid; r <= a.P; r += kLT) a.send_offset[r] = off[E1 + r] - total;
+    if (tid == 0 && off[a.E + 1] != off[a.E]) atomicOr(a.status, MOE_STATUS_BAD_EXPERT);
+  }
+}
+
 }  // namespace
 
 size_t layout_count_lds(int E, int P, int tile) {
@@ -476,13 +672,29 @@ size_t layout_rank_lds(int E, int P, int tile, int K) {
   return (size_t)P * 8 + ints * 4 + (size_t)tile * K * 2;
 }
 
+size_t layout_rank_wave_lds(int E, int P, int tile) {
+  const size_t E1 = (size_t)E + 1, NR = E1 + P;
+  const size_t ngmax = ((size_t)tile + kWave - 1) / kWave;
+  const size_t parts_nr = (size_t)kLT;  // parts * NR <= kLT when NR <= kLT
+  const size_t ints = NR + (NR + 1) + NR + kLW * E1 + kLW + 2 * parts_nr;
+  return (ngmax * P + (size_t)tile) * 8 + ints * 4;
+}
+
+bool layout_rank_wave_fits(int K, int E, int P, int tile) {
+  return (int64_t)tile * K <= kLT && E + 1 + P <= kLT;
+}
+
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(layout_count_kernel, dim3(a.nblk), dim3(kLT), layout_count_lds(a.E, a.P, a.tile),
                      s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(layout_rank_kernel, dim3(a.nblk), dim3(kLT),
-                     layout_rank_lds(a.E, a.P, a.tile, a.K), s, a);
+  if (layout_rank_wave_fits(a.K, a.E, a.P, a.tile))
+    hipLaunchKernelGGL(layout_rank_wave_kernel, dim3(a.nblk), dim3(kLT), layout_rank_wave_lds(a.E, a.P, a.tile),
+                       s, a);
+  else
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(a.nblk), dim3(kLT),
+                       layout_rank_lds(a.E, a.P, a.tile, a.K), s, a);
   return hipGetLastError();
 }
 
