@@ -17,10 +17,11 @@ c_char_p = ctypes.c_char_p
 
 class MoeTuning(ctypes.Structure):
     _fields_ = [("chunks_per_lane", c_int), ("nontemporal", c_int), ("waves_per_block", c_int),
-                ("layout_pairs", c_int)]
+                ("layout_pairs", c_int), ("gather_mode", c_int)]
 
 
-# name -> (restype, argtypes); the functions declared in include/moe_layout.h
+# name -> (restype, argtypes); the functions declared in include/moe_layout.h and
+# include/moe_bench.h (the measurement entry points)
 SIGNATURES = {
     "moe_workspace_size": (c_int, [c_int64, c_int, c_int, c_int, ctypes.POINTER(c_size_t)]),
     "moe_handle_create": (c_int, [ctypes.POINTER(c_void_p), ctypes.POINTER(MoeTuning)]),

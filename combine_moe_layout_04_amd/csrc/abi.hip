@@ -5,6 +5,7 @@
 
 #include "internal.h"
 #include "../../include/moe_layout.h"
+#include "../../include/moe_bench.h"
 
 struct moe_handle_s {
   static constexpr uint32_t kMagic = 0x4D4F454Cu;  // "MOEL"
@@ -192,7 +193,7 @@ int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pa
   // Qwen3-shaped layer (one box, interleaved runs): non-temporal token-row
   // stores take the step from 149.3 to 145.8 us; two segments per wave then
   // gain nothing in the gathers and cost 3 us in each scatter.
-  moe::Tuning t{1, 2, 4, moe::kLayoutThreads};
+  moe::Tuning t{1, 2, 4, moe::kLayoutThreads, 0};
   if (tuning) {
     const int c = tuning->chunks_per_lane, n = tuning->nontemporal, w = tuning->waves_per_block;
     const int lp = tuning->layout_pairs;
@@ -200,6 +201,8 @@ int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pa
     if (n < 0 || n > 2) return MOE_ERR_INVALID_ARG;
     if (!(w == 0 || w == 1 || w == 2 || w == 4 || w == 8)) return MOE_ERR_INVALID_ARG;
     if (!(lp == 0 || lp == 512 || lp == 1024 || lp == 2048 || lp == 4096)) return MOE_ERR_INVALID_ARG;
+    if (tuning->gather_mode != 0 && tuning->gather_mode != 1) return MOE_ERR_INVALID_ARG;
+    t.gather_mode = tuning->gather_mode;
     if (c) t.chunks_per_lane = c;
     t.nontemporal = n;
     if (w) t.waves_per_block = w;
@@ -641,6 +644,6 @@ const char* moe_strerror(int status) {
   }
 }
 
-const char* moe_version(void) { return "moe_layout 0.1 (gfx950)"; }
+const char* moe_version(void) { return "moe_layout 0.2 (gfx950)"; }
 
 }  // extern "C"

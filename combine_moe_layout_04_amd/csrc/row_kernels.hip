@@ -203,6 +203,83 @@ __global__ __launch_bounds__(512) void gather_kernel(GatherArgs a) {
   }
 }
 
+// ---- gather, receive rows staged in LDS ---------------------------------------
+//
+// The same sums as gather_kernel (one wave per (token, segment), float32 in k
+// order from +0.0), with each receive-row segment loaded straight into the
+// wave's slice of LDS by global_load_lds_dwordx4: 64 lanes x 16 bytes land
+// contiguously at the slice's base, no VGPR holds a row in flight, and a
+// group of up to KG rows is in flight together whatever the register budget.
+// The wave then reads its chunks back from LDS for the sum.  Rows of a token
+// are not shared between waves, so the staging buys memory-level parallelism,
+// not reuse.  One segment per wave (chunks_per_lane is ignored).
+
+template <int DT, bool WEIGHTED, bool NTL, bool NTS>
+__global__ __launch_bounds__(512) void gather_lds_kernel(GatherArgs a) {
+  constexpr int V = Elems<DT>::kPerChunk;
+  constexpr int kAux = NTL ? 2 : 0;  // cache policy of the LDS loads: non-temporal
+  extern __shared__ u32x4 stage[];   // [waves per block][KG][64 lanes]
+  const int lane = lane_id();
+  const int wib = (int)(threadIdx.x / kWave);
+  const int wpb = blockDim.x / kWave;
+  const int gw = blockIdx.x * wpb + wib;
+  const int t = gw / a.ngrp;
+  if (t >= a.T) return;  // wave-uniform
+  const int grp = gw - t * a.ngrp;
+  const int j = grp * kWave + lane;
+  const bool valid = j < a.NV;
+
+  const Pairs q = load_pairs(a.recv_pos, WEIGHTED ? a.w : nullptr, t, a.K, a.R);
+  if (grp == 0 && __ballot(q.bad) && lane == 0) atomicOr(a.status, MOE_STATUS_BAD_POSITION);
+
+  u32x4* buf = stage + (size_t)wib * KG * kWave;
+  const u32x4* src = static_cast<const u32x4*>(a.src);
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+
+  for (int kg = 0; kg < a.K; kg += KG) {
+    if (kg > 0) {
+      // the previous group's LDS reads have returned before new rows land
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __asm__ __volatile__("" ::: "memory");
+    }
+#pragma unroll
+    for (int kk = 0; kk < KG; ++kk) {
+      const int k = kg + kk;
+      if (k < a.K) {  // uniform
+        const int p = read_lane_i(q.pos, k);
+        if ((unsigned)p < (unsigned)a.R && valid)
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + (size_t)p * a.NV + j),
+                                           (__attribute__((address_space(3))) void*)(buf + kk * kWave),
+                                           16, 0, kAux);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every staged row has landed
+    __asm__ __volatile__("" ::: "memory");
+#pragma unroll
+    for (int kk = 0; kk < KG; ++kk) {
+      const int k = kg + kk;
+      if (k < a.K) {
+        const int p = read_lane_i(q.pos, k);
+        if ((unsigned)p < (unsigned)a.R && valid) {
+          float f[V];
+          unpack<DT>(buf[kk * kWave + lane], f);
+          if constexpr (WEIGHTED) {
+            const float s = read_lane_f(q.w, k);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] = __fadd_rn(acc[i], __fmul_rn(s, f[i]));
+          } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] = __fadd_rn(acc[i], f[i]);
+          }
+        }
+      }
+    }
+  }
+  if (valid) store_chunk<NTS>(static_cast<u32x4*>(a.dst) + (size_t)t * a.NV + j, pack<DT>(acc));
+}
+
 // ---- token dot (router-weight gradients), optionally with the gather ---------
 
 template <int DT, bool GATHER, bool WEIGHTED, bool NTL, bool NTS>
@@ -353,8 +430,25 @@ hipError_t ga_mode(const GatherArgs& a, const Tuning& t, hipStream_t s) {
   return a.w ? go_gather<DT, CPL, true>(a, t, s) : go_gather<DT, CPL, false>(a, t, s);
 }
 
+template <int DT, bool W>
+hipError_t go_gather_lds(const GatherArgs& a0, const Tuning& tu, hipStream_t s) {
+  GatherArgs a = a0;
+  a.ngrp = groups_per_token(a.NV, 1);
+  const int wpb = tu.waves_per_block;
+  const int64_t waves = (int64_t)a.T * a.ngrp;
+  const dim3 grid((unsigned)((waves + wpb - 1) / wpb)), block(wpb * kWave);
+  const uint32_t lds = (uint32_t)(wpb * KG * kWave * sizeof(u32x4));
+  switch (tu.nontemporal) {
+    case 0: launch_kernel(gather_lds_kernel<DT, W, false, false>, grid, block, lds, s, tu, a); break;
+    case 1: launch_kernel(gather_lds_kernel<DT, W, true, false>, grid, block, lds, s, tu, a); break;
+    default: launch_kernel(gather_lds_kernel<DT, W, true, true>, grid, block, lds, s, tu, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t ga_cpl(const GatherArgs& a, const Tuning& t, hipStream_t s) {
+  if (t.gather_mode == 1) return a.w ? go_gather_lds<DT, true>(a, t, s) : go_gather_lds<DT, false>(a, t, s);
   switch (t.chunks_per_lane) {
     case 2: return ga_mode<DT, 2>(a, t, s);
     case 4: return ga_mode<DT, 4>(a, t, s);

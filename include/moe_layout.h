@@ -7,20 +7,21 @@
  * of one receive buffer in HBM.
  *
  *   "Add an opt-in DeepEP transport for the AutoEP expert all-to-all"
- *   (DeepSpeed PR), sections "Why" and "Scope and safety": dispatch takes the
- *   tokens before top-k expansion together with topk_idx / topk_weights,
- *   copies each token once to every rank that hosts one of its experts,
- *   groups the arrivals by expert, and returns a handle; combine reduces the
- *   weighted sum back to token order.  The backward of a combine is a
- *   dispatch and the backward of a dispatch is a combine, both run with the
- *   forward dispatch's handle.  The review fix on the same page adds that
- *   dispatch returns the received weights and that both backward passes
- *   return the router-weight gradient.
+ *   (DeepSpeed PR), sections "Why" and "Scope and safety": the exchange
+ *   receives tokens before their top-k expansion, together with their expert
+ *   ids and weights; it replicates each token to the ranks that host its
+ *   experts, presents the arrivals grouped by expert, and its combine forms
+ *   the weighted top-k sum in token order again.  Backward needs no entry
+ *   points of its own: each backward pass is the opposite row movement, run
+ *   on the handle the forward dispatch produced.  The review-fix commit on
+ *   that page makes dispatch hand back the received weights and makes both
+ *   backward passes return the router-weight gradient.
  *
- *   "[MoE] Apply router scores before W2 projection" (torchtitan), sections
- *   "Motivation" and "Implementation": with the scores absorbed, dispatch
- *   also returns the per-row scores in the rows' expert-major order, the
- *   rows are scaled in float32 and cast back, and combine is a plain sum.
+ *   "[MoE] Apply router scores before W2 projection" (torchtitan issue),
+ *   sections "Motivation" and "Implementation": when the router scores are
+ *   absorbed into W2's input, dispatch also returns each receive row's score
+ *   in the rows' expert-major order, the scaling is done in float32 and
+ *   rounded back to the row type, and the combine is a plain sum.
  *
  * Conventions (every entry point):
  *   - All tensor pointers are DEVICE pointers; the caller owns every buffer,
@@ -105,6 +106,8 @@ typedef struct moe_tuning {
                            marked non-temporal; 2 (default): token-row stores too    */
   int waves_per_block;  /* wavefronts per workgroup of the row kernels: 0 (= 4), 1, 2, 4, 8 */
   int layout_pairs;     /* (t,k) pairs per layout tile: 0 (= 512), 512, 1024, 2048, 4096      */
+  int gather_mode;      /* receive rows of the gathers (moe_combine, unscaled moe_dispatch_bwd):
+                           0 (default) in registers; 1 staged in LDS by direct loads        */
 } moe_tuning;
 
 typedef struct moe_handle_s* moe_handle_t;
@@ -145,7 +148,7 @@ int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pa
  *              handle's arrays and must outlive every later call on this
  *              handle.  MOE_ERR_WORKSPACE if it is smaller.
  *
- * Definitions (oracle: stable counting sort of the (t,k) pairs by expert):
+ * Definitions (a stable counting sort of the (t,k) pairs by expert id):
  *   recv_pos[t,k] = expert_offset[e] + #{(t',k') < (t,k) lexicographically
  *                    with topk_idx[t',k'] == e},  e = topk_idx[t,k];
  *   expert_offset[e] = sum over e' < e of n_e' (rounded up to the handle's
@@ -173,6 +176,12 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
                hipStream_t stream);
 
 /* Forward dispatch: recv[recv_pos[t,k], :] = x[t, :].
+ * Defined by "Add an opt-in DeepEP transport for the AutoEP expert
+ * all-to-all", sections "What this adds" and "Scope and safety" (tokens
+ * before top-k expansion in, arrivals grouped by expert out), with the
+ * received weights of its review fix (recv_scores) and the float32 row
+ * scaling of "[MoE] Apply router scores before W2 projection",
+ * "Implementation" (scale_rows).
  *
  *   x             [T,H] dtype, 16-byte aligned.
  *   topk_weights  [T,K] float32 or NULL; required when scale_rows or
@@ -189,11 +198,23 @@ int moe_dispatch(moe_handle_t h, const void* x, int dtype, int64_t H,
 
 /* Forward combine: out[t] = round(sum_k w[t,k] * y[recv_pos[t,k]]), or the
  * plain sum when topk_weights is NULL (scores absorbed).  float32, k order.
- *   y [R,H], out [T,H] dtype, 16-byte aligned.                             */
+ * Defined by "Add an opt-in DeepEP transport for the AutoEP expert
+ * all-to-all", section "Scope and safety" (the combine reduces the weighted
+ * sum back to token order), and "[MoE] Apply router scores before W2
+ * projection", "Implementation" (a plain sum once the scores are absorbed).
+ *   y [R,H], out [T,H] dtype, 16-byte aligned.
+ * Errors: MOE_ERR_HANDLE before moe_layout; MOE_ERR_SHAPE / _ALIGNMENT /
+ * _INVALID_ARG for a bad row width, pointer or missing array (checked on the
+ * host, nothing launched); receive rows out of [0,R) set
+ * MOE_STATUS_BAD_POSITION on the device and are skipped.                  */
 int moe_combine(moe_handle_t h, const void* y, int dtype, int64_t H,
                 const float* topk_weights, void* out, hipStream_t stream);
 
-/* Backward of moe_combine (a dispatch of the output gradient):
+/* Backward of moe_combine (a dispatch of the output gradient), per
+ * "Add an opt-in DeepEP transport for the AutoEP expert all-to-all",
+ * section "Scope and safety" (the gradient of a combine is a dispatch on the
+ * forward's handle) and the same page's review fix (the weight gradient is
+ * returned, never dropped):
  *   grad_y[recv_pos[t,k]] = round(w[t,k] * grad_out[t])  (copy if no weights)
  *   grad_w[t,k] = <grad_out[t], y[recv_pos[t,k]]>        (if grad_w != NULL)
  * grad_w needs topk_weights and y.  The dot product is float32 in a fixed
@@ -211,7 +232,12 @@ int moe_combine_bwd(moe_handle_t h, const void* grad_out, int dtype, int64_t H,
                     const float* topk_weights, const void* y, void* grad_y,
                     float* grad_w, hipStream_t stream);
 
-/* Backward of moe_dispatch (a combine of the receive-row gradient):
+/* Backward of moe_dispatch (a combine of the receive-row gradient), per
+ * "Add an opt-in DeepEP transport for the AutoEP expert all-to-all",
+ * section "Scope and safety" (the gradient of a dispatch is a combine on the
+ * forward's handle); with scores absorbed, "[MoE] Apply router scores before
+ * W2 projection", "Implementation" and "Tests and verifications" (the score
+ * gradient flows through W2's input scaling):
  *   grad_x[t] = round(sum_k [w[t,k] *] grad_recv[recv_pos[t,k]])
  *   grad_s[t,k] = <grad_recv[recv_pos[t,k]], x[t]>        (if grad_s != NULL)
  * Pass topk_weights iff the forward dispatch scaled its rows (the scaling is
@@ -297,9 +323,10 @@ int moe_handle_check(moe_handle_t h, hipStream_t stream, int* device_status);
  * The exchange calls issued on it use at most that many CUs, and a GEMM on a
  * stream with the other CUs runs beside them: the analogue of the SM budget
  * of the pages' transport kernels ("Add an opt-in DeepEP transport for the
- * AutoEP expert all-to-all", section "Choosing the SM budget": the exchange
- * competes with the expert GEMM for SMs, so the budget was chosen on whole
- * steps; its follow-up list names communication/compute overlap).  CU
+ * AutoEP expert all-to-all", section "Choosing the SM budget": too few SMs
+ * slow the exchange itself and too many slow the GEMMs beside it, so the
+ * budget is a whole-step trade-off; the page's follow-up work lists
+ * overlapping the exchange with compute).  CU
  * indices are the HIP runtime's, numbered round-robin over the XCDs, so a
  * range of consecutive indices spreads evenly over them; the runtime refuses
  * a mask that leaves an XCD without a CU, so cu_count is at least the XCD
@@ -309,27 +336,6 @@ int moe_handle_check(moe_handle_t h, hipStream_t stream, int* device_status);
  * with moe_stream_destroy.                                                 */
 int moe_stream_create_cu_budget(int cu_first, int cu_count, hipStream_t* out);
 int moe_stream_destroy(hipStream_t stream);
-
-/* Plain device copy of `bytes` (multiple of 16, 16-byte aligned pointers):
- * the reference kernel for calibrating HBM traffic counters against a known
- * byte count.  Not part of the method.                                    */
-int moe_bench_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
-
-/* Measurement hook (not part of the method).  The next kernel that a row
- * call on this handle launches (moe_dispatch, moe_combine, moe_combine_bwd,
- * moe_dispatch_bwd or a staged call; the first kernel of a call that has
- * two) is launched with hipExtLaunchKernel: stop is bound to that kernel's
- * completion, and start, when not NULL, is recorded just before it, so
- * that their elapsed time is the kernel's own execution, without the launch
- * latency that events recorded around the call include.  A stop alone costs
- * nothing measurable (consecutive stops give exact periods); a start adds a
- * marker to the stream (about 3 us of GPU time on MI355X).  One-shot: the
- * launch consumes them.  Both NULL disarms.  The events belong to the
- * caller, were created on the call's device, and must stay alive until the
- * call's stream has passed them.  Meant for eager launches: its use under
- * graph capture is untested.  Returns MOE_ERR_INVALID_ARG for a bad handle,
- * or a start without a stop. */
-int moe_time_next_kernel(moe_handle_t h, hipEvent_t start, hipEvent_t stop);
 
 /* Message for a status code (static string). */
 const char* moe_strerror(int status);

@@ -10,6 +10,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_layout.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -21,8 +23,8 @@ def L():
     return _lib.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(headers=HEADERS):
+    text = "".join(open(h).read() for h in headers)
     return sorted(set(re.findall(r"^(?:int|const char\*)\s+(moe_\w+)\s*\(", text, re.M)))
 
 
@@ -36,10 +38,17 @@ FAKE = 1 << 20          # a 256-aligned address that validation never dereferenc
 
 
 def test_header_declares_the_method_entry_points():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for n in ("moe_layout", "moe_dispatch", "moe_combine", "moe_dispatch_bwd", "moe_combine_bwd",
               "moe_handle_create", "moe_handle_destroy", "moe_workspace_size"):
         assert n in names
+
+
+def test_measurement_hooks_are_outside_the_method_header():
+    method = declared_functions([HEADER])
+    bench = declared_functions([os.path.join(ROOT, "include", "moe_bench.h")])
+    assert bench == ["moe_bench_copy", "moe_time_next_kernel"]
+    assert not set(bench) & set(method)
 
 
 def test_every_declared_function_is_exported(L):
@@ -87,9 +96,10 @@ def test_handle_lifecycle_and_tuning(L):
     assert L.moe_handle_destroy(None) == C["MOE_ERR_INVALID_ARG"]
     assert L.moe_handle_create(None, None) == C["MOE_ERR_INVALID_ARG"]
     for bad in (MoeTuning(3, 0, 0, 0), MoeTuning(0, 3, 0, 0), MoeTuning(0, 0, 3, 0),
-                MoeTuning(0, 0, 0, 300), MoeTuning(0, 0, 0, 8192)):
+                MoeTuning(0, 0, 0, 300), MoeTuning(0, 0, 0, 8192), MoeTuning(0, 0, 0, 0, 2),
+                MoeTuning(0, 0, 0, 0, -1)):
         assert L.moe_handle_create(ctypes.byref(h), ctypes.byref(bad)) == C["MOE_ERR_INVALID_ARG"]
-    good = MoeTuning(2, 2, 8, 2048)
+    good = MoeTuning(2, 2, 8, 2048, 1)
     assert L.moe_handle_create(ctypes.byref(h), ctypes.byref(good)) == C["MOE_OK"]
     assert L.moe_handle_destroy(h) == C["MOE_OK"]
 
