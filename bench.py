@@ -25,6 +25,12 @@ That step measured 140.4 us with 3 sets, 146.8 with 8, 150.0 with 16 and
 150.2-150.6 with 24 to 48.  ``--warm`` chains the real tensors instead
 (combine reads what dispatch wrote) as a secondary figure.
 
+Timing: set-up runs one untimed step on every buffer set, then the warmup
+steps; the headline is K steps of plain launches bracketed by
+synchronisations (wall clock, no event inside).  An event pass of K more
+steps in the same rotation then takes the dominant kernel's own start and
+stop events and the step distribution; it never feeds `value`.
+
 Prints ONE JSON line.  ``--gpus N`` with N > 1 is not supported (the path is
 one GPU's share of the exchange).
 """
@@ -63,15 +69,19 @@ def parse():
     ap.add_argument("--nontemporal", type=int, default=2)
     ap.add_argument("--waves-per-block", type=int, default=0)
     ap.add_argument("--layout-pairs", type=int, default=0)
+    ap.add_argument("--gather-mode", type=int, default=0,
+                    help="receive rows of the gathers: 0 in registers, 1 staged in LDS")
     ap.add_argument("--events", choices=["kernel", "all", "none"], default="kernel",
-                    help="HIP events in the timed region. kernel: the dominant kernel's own start and "
-                         "stop on every --kernel-every-th step, and a free stop event bound to each "
-                         "step's last kernel (step times); all: also hipEventRecord around every call, "
-                         "and the dominant kernel timed on every step (diagnostic: the records cost "
-                         "GPU time); none: wall time only")
-    ap.add_argument("--kernel-every", type=int, default=8,
-                    help="with --events kernel, time the dominant kernel on every n-th timed step "
-                         "(its start event is a stream marker: about 3 us of GPU time)")
+                    help="HIP events of the event pass, which repeats the timed steps after the "
+                         "headline loop (the headline loop itself records no event). kernel: the "
+                         "dominant kernel's own start and stop on every --kernel-every-th step, and a "
+                         "free stop event bound to each step's last kernel (step times); all: also "
+                         "hipEventRecord around every call, and the dominant kernel timed on every "
+                         "step (per-call diagnostics; the records cost GPU time); none: no event pass")
+    ap.add_argument("--kernel-every", type=int, default=2,
+                    help="in the event pass, time the dominant kernel on every n-th step (its start "
+                         "event is a stream marker, about 3 us of GPU time; step times are taken "
+                         "over the other steps)")
     ap.add_argument("--staged", action="store_true",
                     help="staged exchange: send buffer per destination partition, receiver-side "
                          "expansion, two-level combine")
@@ -246,7 +256,9 @@ def sources_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_moe_layout_04_amd", "csrc")
     paths = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
-    for path in paths + [os.path.join(ROOT, "include", "moe_layout.h")]:
+    inc = os.path.join(ROOT, "include")
+    headers = sorted(os.path.join(inc, f) for f in os.listdir(inc) if f.endswith(".h"))
+    for path in paths + headers:
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as fh:
             h.update(fh.read())
@@ -573,7 +585,7 @@ def main():
                 out=empty_rows(cfg.T),
                 ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
                 h=M.Handle(args.chunks_per_lane, args.nontemporal, args.waves_per_block, args.layout_pairs,
-                           pad_multiple=m)))
+                           pad_multiple=m, gather_mode=args.gather_mode)))
         s["grad_y"] = empty_rows(RC)
         s["grad_w"] = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device=dev)
         s["grad_x"] = empty_rows(cfg.T)
@@ -665,34 +677,45 @@ def main():
         else:
             raise ValueError(kind)
 
-    def step(s, i=None):
-        # i: timed step index.  On a timed step the dominant call's kernel
-        # may record its own start and stop, the last call's kernel binds the
-        # step's stop event, and with --events all every call is bracketed.
+    def step(s, ev=None, i=None):
+        # ev: the event pass's events, i: its step index.  The dominant
+        # call's kernel may record its own start and stop, the last call's
+        # kernel binds the step's stop event, and with --events all every
+        # call is bracketed by records.  The headline loop passes no events.
         for j, (_, kind, p, _) in enumerate(calls):
             slot = None
-            if i is not None:
+            if ev is not None:
                 h = s["pass"][p]["h"]
-                if j == d and i in kslot:
-                    r = kslot[i]
-                    M.moe_time_next_kernel(h, kev.ev[2 * r].value, kev.ev[2 * r + 1].value)
-                if j == ncall - 1 and bev is not None:
-                    M.moe_time_next_kernel(h, None, bev.ev[i].value)
-                slot = slot_of.get(j)
+                if j == d and i in ev["kslot"]:
+                    r = ev["kslot"][i]
+                    M.moe_time_next_kernel(h, ev["kev"].ev[2 * r].value, ev["kev"].ev[2 * r + 1].value)
+                if j == ncall - 1 and ev["bev"] is not None:
+                    M.moe_time_next_kernel(h, None, ev["bev"].ev[i].value)
+                slot = ev["slot_of"].get(j)
                 if slot is not None:
-                    hev.record(per_step * i + 2 * slot, stream)
+                    ev["hev"].record(ev["per_step"] * i + 2 * slot, stream)
             run_call(s, kind, p)
             if slot is not None:
-                hev.record(per_step * i + 2 * slot + 1, stream)
+                ev["hev"].record(ev["per_step"] * i + 2 * slot + 1, stream)
 
-    slot_of, kslot, bev = {}, {}, None
     d = names.index(dom)
     assert d != ncall - 1, "the step's last call carries the step-boundary event"
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    # Set-up, untimed: every buffer set runs one step, so that no set is
+    # first touched inside a timed region.  Then the warmup steps, and the
+    # timed steps continue the same rotation: every set is last touched
+    # nsets - 1 steps before its next use.
+    for s in sets:
+        step(s)
     for i in range(args.warmup):
         step(sets[i % nsets])
-    for s in sets[:min(nsets, args.warmup)]:  # the sets the warmup ran
+    for s in sets:
         for q in s["pass"]:
             assert q["h"].check() == 0
+    first = args.warmup % nsets
+
+    def set_of(i):
+        return sets[(first + i) % nsets]
 
     if args.overlap:
         overlap_run(args, cfg, step, sets, nsets, calls, n_send, pad_rows)
@@ -713,63 +736,82 @@ def main():
             with torch.cuda.graph(g):
                 step(s)
             graphs.append(g)
+        for g in graphs:
+            g.replay()
         for i in range(args.warmup):
             graphs[i % nsets].replay()
         torch.cuda.synchronize()
-
-    K = args.steps
     eager = graphs is None
-    events = args.events if eager else "none"
-    # --events all: hipEventRecord around every call
-    timed = list(range(ncall)) if events == "all" else []
-    slot_of = {j: r for r, j in enumerate(timed)}
-    per_step = 2 * len(timed)
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    hev = HipEvents(per_step * K)
-    # the dominant kernel's own start and stop, on a sample of the timed steps
-    every = 1 if events == "all" else max(1, args.kernel_every)
-    ksteps = [i for i in range(K) if i % every == 0] if events != "none" else []
-    kslot = {i: r for r, i in enumerate(ksteps)}
-    kev = HipEvents(2 * len(ksteps))
-    # step boundaries: a stop event bound to each step's last kernel (free),
-    # or, for graph replays, a record after each replay
-    bev = HipEvents(K) if events != "none" else None
-    sev = HipEvents(K + 1 if not eager else 0)
+
+    def run_steps(K, start, ev=None):
+        # steps start .. start+K-1 of the rotation
+        for i in range(K):
+            if not eager:
+                if ev is not None:
+                    ev["sev"].record(i, stream)
+                graphs[(first + start + i) % nsets].replay()
+            else:
+                step(set_of(start + i), ev, i)
+        if not eager and ev is not None:
+            ev["sev"].record(K, stream)
+
+    # The headline: K steps of plain launches (or graph replays), bracketed
+    # by synchronisations, wall clock only.  No event is recorded or bound
+    # inside it.
+    K = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        if not eager:
-            sev.record(i, stream)
-            graphs[i % nsets].replay()
-        else:
-            step(sets[i % nsets], i)
-    if not eager:
-        sev.record(K, stream)
+    run_steps(K, 0)
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
     host_us = (t_enq - t0) * 1e6 / K
 
-    # per-call event times (--events all only)
-    call_ms = {names[j]: [hev.elapsed_ms(per_step * i + 2 * r, per_step * i + 2 * r + 1) for i in range(K)]
-               for r, j in enumerate(timed)}
-    hev.close()
-    kern_us = [kev.elapsed_ms(2 * r, 2 * r + 1) * 1e3 for r in range(len(ksteps))] or None
-    kev.close()
+    # The event pass: K more steps of the same rotation, with
+    # HIP events on the stream the library launches on.  It gives the
+    # dominant kernel's own duration (its start and stop events, on every
+    # other step) and the step distribution (a stop event bound to each
+    # step's last kernel, free; taken over the steps without a start marker,
+    # which costs about 3 us).  Its wall time is reported beside the
+    # headline's, never as it.
+    events = args.events if eager else ("none" if args.events == "none" else "graph")
+    ev = None
+    ev_ms_per_step = None
+    kern_us, call_ms, st = None, {}, None
+    ksteps = []
+    if events != "none":
+        timed = list(range(ncall)) if events == "all" else []  # --events all: records around every call
+        every = 1 if events == "all" else max(1, args.kernel_every)
+        ksteps = [i for i in range(K) if i % every == 0] if events in ("kernel", "all") else []
+        ev = {"slot_of": {j: r for r, j in enumerate(timed)}, "per_step": 2 * len(timed),
+              "kslot": {i: r for r, i in enumerate(ksteps)}}
+        ev["hev"] = HipEvents(ev["per_step"] * K)
+        ev["kev"] = HipEvents(2 * len(ksteps))
+        ev["bev"] = HipEvents(K) if eager else None
+        ev["sev"] = HipEvents(K + 1 if not eager else 0)
+        torch.cuda.synchronize()
+        e0 = time.perf_counter()
+        run_steps(K, K, ev)  # the rotation continues where the headline left it
+        torch.cuda.synchronize()
+        ev_ms_per_step = (time.perf_counter() - e0) * 1e3 / K
+        call_ms = {names[j]: [ev["hev"].elapsed_ms(ev["per_step"] * i + 2 * r, ev["per_step"] * i + 2 * r + 1)
+                              for i in range(K)] for r, j in enumerate(timed)}
+        kern_us = [ev["kev"].elapsed_ms(2 * r, 2 * r + 1) * 1e3 for r in range(len(ksteps))] or None
+        if eager and K > 1:   # end of step i-1's last kernel to end of step i's
+            clean = [i for i in range(1, K) if i not in ev["kslot"]] or list(range(1, K))
+            st = np.array([ev["bev"].elapsed_ms(i - 1, i) for i in clean]) * 1e3
+        elif not eager:
+            st = np.array([ev["sev"].elapsed_ms(i, i + 1) for i in range(K)]) * 1e3
+        for k in ("hev", "kev", "bev", "sev"):
+            if ev[k] is not None:
+                ev[k].close()
+
     avg_us = {n: float(np.mean(v)) * 1e3 for n, v in call_ms.items()}
     med_us = {n: float(np.median(v)) * 1e3 for n, v in call_ms.items()}
-    st = None
-    if bev is not None and K > 1:   # end of step i-1's last kernel to end of step i's
-        st = np.array([bev.elapsed_ms(i - 1, i) for i in range(1, K)]) * 1e3
-    elif not eager:
-        st = np.array([sev.elapsed_ms(i, i + 1) for i in range(K)]) * 1e3
     step_us = None if st is None else {
         "median": round(float(np.median(st)), 2), "p10": round(float(np.percentile(st, 10)), 2),
-        "p90": round(float(np.percentile(st, 90)), 2)}
-    if bev is not None:
-        bev.close()
-    sev.close()
+        "p90": round(float(np.percentile(st, 90)), 2), "n": int(len(st))}
     per_pass = None
     if cfg.absorbed and len(avg_us) == ncall:
         # each forward pass, and each replay + backward
@@ -855,11 +897,13 @@ def main():
             "index_bytes_per_step": index_bytes(cfg, args.staged, n_send, pad_rows),
             **({} if m == 1 else {"pad_multiple": m, "padding_rows": pad_rows}),
             "host_enqueue_us_per_step": round(host_us, 1),
+            "event_pass_us_per_step": None if ev_ms_per_step is None else round(ev_ms_per_step * 1e3, 2),
             "step_us": step_us,
             **({} if per_pass is None else {"per_pass_us": per_pass}),
-            "timing": ("hip graph replay" if graphs is not None else "eager launches") +
-                      f", events: {events}" + (f" (dominant kernel timed on {len(ksteps)} of {K} steps)"
-                                               if ksteps else ""),
+            "timing": ("hip graph replays" if graphs is not None else "eager launches") +
+                      f"; headline loop without events, set-up touches all {nsets} sets first; event pass "
+                      f"(same {K} steps): {events}" +
+                      (f", dominant kernel timed on {len(ksteps)} of {K} steps" if ksteps else ""),
             **({} if not args.staged else {
                 "exchange": "staged",
                 "n_send": n_send,
@@ -873,7 +917,8 @@ def main():
                 "direct_step_bytes_per_s_GBps": round(direct_b / (ms_per_step * 1e-3) / 1e9, 2),
             }),
             "tuning": {"chunks_per_lane": args.chunks_per_lane, "nontemporal": args.nontemporal,
-                       "waves_per_block": args.waves_per_block, "layout_pairs": args.layout_pairs},
+                       "waves_per_block": args.waves_per_block, "layout_pairs": args.layout_pairs,
+                       "gather_mode": args.gather_mode},
             "sources_sha256": sources_hash(),
         },
         "roofline": None if achieved is None else {
@@ -888,7 +933,7 @@ def main():
             "avg_launch_us": round(dom_us, 2),
             "median_launch_us": round(float(np.median(kern_us)), 2),
             "launch_timing": f"the kernel's own start and stop events (hipExtLaunchKernel), on {len(ksteps)} "
-                             f"of the {K} timed steps",
+                             f"of the {K} steps of the event pass",
             **({} if dom not in avg_us else {"call_interval_avg_us": round(avg_us[dom], 2)}),
             "achievable_copy_GBps": ceiling,
             "frac_of_achievable": None if ceiling is None else round(achieved / ceiling, 4),
