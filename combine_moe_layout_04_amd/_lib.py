@@ -31,6 +31,8 @@ SIGNATURES = {
     "moe_handle_destroy": (c_int, [c_void_p]),
     "moe_layout": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int, c_int, c_int, c_void_p,
                            c_size_t, c_void_p]),
+    "moe_layout_noalloc": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int, c_int, c_int, c_void_p,
+                                   c_size_t, c_void_p]),
     "moe_dispatch": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_void_p, c_int, c_void_p,
                              c_void_p, c_void_p]),
     "moe_combine": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_void_p, c_void_p, c_void_p]),

@@ -1,6 +1,8 @@
 // C ABI of libmoe_layout.so: host-side validation, the workspace plan, the
 // opaque handle and stream-ordered launches.  Every argument error is caught
 // here, before any HIP call, so a rejected call launches nothing.
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "internal.h"
@@ -223,8 +225,58 @@ int moe_handle_destroy(moe_handle_t h) {
   return MOE_OK;
 }
 
-int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K, int E,
-               int P, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- the no-allocation layout's scratch ---------------------------------------
+//
+// moe_layout_noalloc keeps the layout's per-tile histogram (its only scratch:
+// written by the count kernel, read by the rank kernel, dead afterwards) in
+// this file-scope device array instead of the caller's workspace.  Every GPU
+// the library runs on holds its own copy until the process ends.  In host code
+// `scratch` is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only that
+// address is ever handed to a kernel.
+constexpr size_t kScratchBytes = size_t(2) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch array's address on the device `stream` runs on.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return MOE_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return MOE_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = 0;
+      if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev && hipSetDevice(cur) != hipSuccess) return MOE_ERR_HIP;
+      if (e != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+// moe_layout and moe_layout_noalloc.  static_hist: the histogram goes to the
+// per-device scratch array, and the workspace only needs the handle's arrays
+// (the sections before the histogram).
+int layout_call(moe_handle_s* h, const void* topk_idx, int itype, int64_t T, int K, int E, int P,
+                void* workspace, size_t workspace_bytes, bool static_hist, hipStream_t stream) {
   if (!valid_handle(h)) return MOE_ERR_INVALID_ARG;
   int st = check_shape(T, K, E, P);
   if (st != MOE_OK) return st;
@@ -234,10 +286,18 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
   if (!aligned(workspace, 256)) return MOE_ERR_ALIGNMENT;
   if (T > 0 && !aligned(topk_idx, itype == MOE_I32 ? 4 : 8)) return MOE_ERR_ALIGNMENT;
   const moe::WsLayout sized = moe::plan_workspace(T, K, E, P, moe::kLayoutThreads, h->pad);
-  if (workspace_bytes < sized.total) return MOE_ERR_WORKSPACE;
+  // the histogram is the workspace's last section: without it, the handle's arrays
+  if (workspace_bytes < (static_hist ? sized.hist : sized.total)) return MOE_ERR_WORKSPACE;
   // the handle's tile size: never more tiles than the default plan sizes for
   moe::WsLayout plan = moe::plan_workspace(T, K, E, P, h->tune.layout_pairs, h->pad);
   plan.hist = sized.hist;
+  int* hist = nullptr;
+  if (static_hist) {
+    if ((size_t)(E + 1 + P) * (size_t)plan.nblk * sizeof(int) > kScratchBytes) return MOE_ERR_SCRATCH;
+    void* p = nullptr;
+    if ((st = scratch_address(stream, &p)) != MOE_OK) return st;
+    hist = static_cast<int*>(p);
+  }
 
   h->has_layout = false;
   h->T = T;
@@ -260,7 +320,7 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
   a.R = (int)h->R;
   a.nblk = plan.nblk;
   a.tile = plan.tile;
-  a.hist = ws_ptr<int>(h, plan.hist);
+  a.hist = static_hist ? hist : ws_ptr<int>(h, plan.hist);
   a.tok_mask = ws_ptr<unsigned long long>(h, plan.tok_mask);
   a.num_tokens_per_expert = ws_ptr<int>(h, plan.num_tokens_per_expert);
   a.num_tokens_per_rank = ws_ptr<int>(h, plan.num_tokens_per_rank);
@@ -277,6 +337,20 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
   const int rc = hip_status(moe::launch_layout(a, stream));
   if (rc == MOE_OK) h->has_layout = true;
   return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K, int E,
+               int P, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return layout_call(h, topk_idx, itype, T, K, E, P, workspace, workspace_bytes, false, stream);
+}
+
+int moe_layout_noalloc(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K, int E,
+                       int P, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return layout_call(h, topk_idx, itype, T, K, E, P, workspace, workspace_bytes, true, stream);
 }
 
 int moe_dispatch(moe_handle_t h, const void* x, int dtype, int64_t H, const float* topk_weights,
@@ -640,6 +714,8 @@ const char* moe_strerror(int status) {
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
     case MOE_ERR_HANDLE: return "bad handle, or a row call before moe_layout";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_SCRATCH:
+      return "the layout's histogram exceeds the static scratch of moe_layout_noalloc (2 MiB); use moe_layout";
     default: return "unknown status";
   }
 }

@@ -63,6 +63,7 @@ extern "C" {
 #define MOE_ERR_WORKSPACE     -5  /* workspace smaller than moe_workspace_size() */
 #define MOE_ERR_HANDLE        -6  /* bad handle, or a data call before moe_layout */
 #define MOE_ERR_HIP           -7  /* a HIP runtime call failed */
+#define MOE_ERR_SCRATCH       -8  /* moe_layout_noalloc: the histogram exceeds its static scratch */
 
 /* ---- element and index types ------------------------------------------- */
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
@@ -174,6 +175,26 @@ int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pa
 int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K,
                int E, int P, void* workspace, size_t workspace_bytes,
                hipStream_t stream);
+
+/* moe_layout for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and handle as moe_layout; the difference is where the
+ * layout's scratch lives.  moe_layout keeps its per-tile histogram in the
+ * caller's workspace; this call keeps it in a static array inside the
+ * library, one per GPU, held until the process ends, so the workspace only
+ * has to hold the handle's arrays (moe_workspace_size() bytes always
+ * suffice; the histogram section at their end is not touched).  The call
+ * itself allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  Limit: the histogram, (E+1+P) * tiles * 4 bytes (tiles = about
+ * T*K/512, at most a few hundred), must fit in 2 MiB; a larger shape is
+ * refused on the host with MOE_ERR_SCRATCH, before any launch.  Every call
+ * on one GPU shares that GPU's array: layouts that overlap in time on one
+ * GPU (two streams, or two host threads) race on it and must be ordered by
+ * the caller; each call writes every histogram entry it reads, so nothing
+ * has to be cleared between calls.                                        */
+int moe_layout_noalloc(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K,
+                       int E, int P, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /* Forward dispatch: recv[recv_pos[t,k], :] = x[t, :].
  * Defined by "Add an opt-in DeepEP transport for the AutoEP expert

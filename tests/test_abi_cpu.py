@@ -79,6 +79,31 @@ def test_workspace_size_rules(L):
     assert f(16, 8, 128, 8, None) == C["MOE_ERR_INVALID_ARG"]
 
 
+def test_noalloc_layout_host_checks(L):
+    """moe_layout_noalloc: the host-side refusals, before any HIP call.  Its
+    workspace holds the handle's arrays only (the histogram section that ends
+    moe_workspace_size's count is not needed); a histogram beyond its 2 MiB
+    static scratch is refused with MOE_ERR_SCRATCH."""
+    h = ctypes.c_void_p()
+    assert L.moe_handle_create(ctypes.byref(h), None) == 0
+    try:
+        n = ctypes.c_size_t()
+        T, K, E, P = 4096, 8, 128, 8
+        assert L.moe_workspace_size(T, K, E, P, ctypes.byref(n)) == 0
+        hist = (E + 1 + P) * 64 * 4            # 64 tiles of 512 pairs
+        f = L.moe_layout_noalloc
+        assert f(None, FAKE, 0, T, K, E, P, FAKE, n.value, None) == C["MOE_ERR_INVALID_ARG"]
+        assert f(h, FAKE, 0, T, K, 130, P, FAKE, n.value, None) == C["MOE_ERR_SHAPE"]
+        assert f(h, FAKE, 0, T, K, E, P, FAKE + 8, n.value, None) == C["MOE_ERR_ALIGNMENT"]
+        assert f(h, FAKE, 0, T, K, E, P, FAKE, n.value - hist - 257, None) == C["MOE_ERR_WORKSPACE"]
+        assert L.moe_layout(h, FAKE, 0, T, K, E, P, FAKE, n.value - 1, None) == C["MOE_ERR_WORKSPACE"]
+        # 2^21 tokens, K = 1, E = 1024, P = 64: about 700 tiles x 1089 columns x 4 bytes > 2 MiB
+        assert f(h, FAKE, 0, 1 << 21, 1, 1024, 64, FAKE, 1 << 40, None) == C["MOE_ERR_SCRATCH"]
+        assert b"static" in L.moe_strerror(C["MOE_ERR_SCRATCH"])
+    finally:
+        L.moe_handle_destroy(h)
+
+
 def test_workspace_holds_the_handle_arrays(L):
     # T*K positions, two inverse maps, T*P slots and flags, counts and offsets
     n = ctypes.c_size_t()
