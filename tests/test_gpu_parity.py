@@ -147,6 +147,45 @@ def test_layout_shapes(T, K, E, P, distinct, layout_pairs):
     check_layout(h, O.layout(idx, E, P))
 
 
+MORE_SHAPES = [  # (T, K, E, P, id dtype)
+    (8192, 8, 128, 8, np.int32),     # the DiffusionGemma token count
+    (8192, 8, 128, 8, np.int64),
+    (8193, 8, 128, 8, np.int32),
+    (16384, 4, 512, 64, np.int32),   # K = 4, E = 512, P = 64
+    (16384, 4, 512, 64, np.int64),
+    (100, 32, 64, 16, np.int32),     # K = 32
+    (1, 4, 4, 2, np.int64),          # one token
+    (1000, 8, 8, 8, np.int32),       # K = E: every token on every partition
+    (300, 12, 96, 24, np.int32),     # K = 12, most tokens on some partitions only
+]
+
+
+@pytest.mark.parametrize("T,K,E,P,dt", MORE_SHAPES)
+def test_layout_more_shapes(T, K, E, P, dt):
+    say(f"layout T={T} K={K} E={E} P={P} {np.dtype(dt).name}")
+    rng = np.random.default_rng(T + 31 * K + E)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(dt)
+    h = M.moe_layout(torch.from_numpy(idx).to(DEV), E, P)
+    assert h.check() == 0
+    check_layout(h, O.layout(idx, E, P))
+
+
+def test_layout_flags_bad_ids_at_k8():
+    """Out-of-range ids at K = 8: flagged, and every position stays a
+    bijection onto [0, T*K) with the bad pairs last."""
+    T, K, E, P = 700, 8, 64, 8
+    rng = np.random.default_rng(5)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    idx[3, 5] = E + 7
+    idx[650, 0] = -2
+    h = M.moe_layout(torch.from_numpy(idx).to(DEV), E, P)
+    assert h.check() & 1
+    pos = h.field("recv_pos").cpu().numpy()
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(T * K))
+    eo = h.field("expert_offset").cpu().numpy()
+    assert eo[E] == T * K - 2 and pos[3, 5] >= eo[E] and pos[650, 0] >= eo[E]
+
+
 def test_layout_all_on_one_expert_and_empty_partitions():
     T, K, E, P = 3000, 1, 64, 16
     idx = np.full((T, K), 37, np.int32)
