@@ -75,7 +75,8 @@ def parse():
                     help="HIP events of the event pass, which repeats the timed steps after the "
                          "headline loop (the headline loop itself records no event). kernel: the "
                          "dominant kernel's own start and stop on every --kernel-every-th step, and a "
-                         "free stop event bound to each step's last kernel (step times); all: also "
+                         "stop event bound to each step's last kernel (step times; it idles the queue "
+                         "about 4.5 us); all: also "
                          "hipEventRecord around every call, and the dominant kernel timed on every "
                          "step (per-call diagnostics; the records cost GPU time); none: no event pass")
     ap.add_argument("--kernel-every", type=int, default=2,
@@ -772,7 +773,8 @@ def main():
     # HIP events on the stream the library launches on.  It gives the
     # dominant kernel's own duration (its start and stop events, on every
     # other step) and the step distribution (a stop event bound to each
-    # step's last kernel, free; taken over the steps without a start marker,
+    # step's last kernel (it idles the queue about 4.5 us before the next
+    # kernel); taken over the steps without a start marker,
     # which costs about 3 us).  Its wall time is reported beside the
     # headline's, never as it.
     events = args.events if eager else ("none" if args.events == "none" else "graph")
