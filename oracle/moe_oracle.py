@@ -7,14 +7,15 @@ library never calls it and shares no code with it.
 It is numpy, written to be read against the pages:
 
 * "Add an opt-in DeepEP transport for the AutoEP expert all-to-all"
-  (DeepSpeed PR), sections "Why" and "Scope and safety": the exchange takes
-  tokens before top-k expansion, copies each token to every rank that hosts
-  one of its experts, groups what arrives by expert, and its combine reduces
-  the weighted sum back to token order.  The backward of a combine is a
-  dispatch and the backward of a dispatch is a combine, both run against the
-  handle of the forward dispatch.  The review fix commit adds that dispatch
-  returns the received weights and that both backward passes return the
-  router-weight gradient.
+  (DeepSpeed PR), sections "Why" and "Scope and safety": the input is the
+  tokens before their top-k expansion with their expert ids and weights;
+  every rank hosting one of a token's experts receives that token, arrivals
+  are grouped by expert, and the combine forms the weighted top-k sum in
+  token order again.  Each backward pass is the opposite row movement on the
+  forward's handle (spreading the output gradient for the combine, summing
+  receive-row gradients for the dispatch).  The page's review-fix commit
+  makes dispatch hand back the received weights and both backward passes
+  return the router-weight gradient.
 * "[MoE] Apply router scores before W2 projection" (torchtitan), sections
   "Motivation" and "Implementation": with scores absorbed, the per-row
   scores are gathered expert-major with the same permutation as the rows,
