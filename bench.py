@@ -219,6 +219,18 @@ KERNEL_SOURCES = {False: ("row_kernels.hip", ("scatter_kernel", "go_scatter"), (
                   True: ("staged_kernels.hip", ("expand_kernel", "go_expand"), ("device_common.h", "pad_fill.h"))}
 
 
+def rotation(nsets, warmup, steps):
+    """Buffer-set indices of each phase of a run: set-up (every set once),
+    warmup, the headline steps and the event-pass steps.  The timed phases
+    continue the warmup's rotation, so a set used by a timed step was last
+    used nsets - 1 steps earlier (with at least as many steps run before it)."""
+    first = warmup % nsets
+    return {"setup": list(range(nsets)),
+            "warmup": [i % nsets for i in range(warmup)],
+            "headline": [(first + i) % nsets for i in range(steps)],
+            "event": [(first + steps + i) % nsets for i in range(steps)]}
+
+
 def dominant_call(cfg, staged=False):
     name = DOMINANT[staged]
     if not cfg.absorbed:
@@ -706,16 +718,17 @@ def main():
     # first touched inside a timed region.  Then the warmup steps, and the
     # timed steps continue the same rotation: every set is last touched
     # nsets - 1 steps before its next use.
-    for s in sets:
-        step(s)
-    for i in range(args.warmup):
-        step(sets[i % nsets])
+    order = rotation(nsets, args.warmup, args.steps)
+    for j in order["setup"]:
+        step(sets[j])
+    for j in order["warmup"]:
+        step(sets[j])
     for s in sets:
         for q in s["pass"]:
             assert q["h"].check() == 0
     first = args.warmup % nsets
 
-    def set_of(i):
+    def set_of(i):  # timed step i (headline, then event pass) of the rotation
         return sets[(first + i) % nsets]
 
     if args.overlap:

@@ -104,3 +104,19 @@ def test_sources_hash_names_the_code(tmp_path, monkeypatch):
     assert bench.sources_hash() == h0
     (csrc / "a.hip").write_text("// a, changed\n")
     assert bench.sources_hash() != h0
+
+
+@pytest.mark.parametrize("nsets,warmup,steps", [(18, 5, 20), (18, 20, 200), (5, 10, 50), (3, 0, 7), (1, 2, 3)])
+def test_rotation_touches_every_set_first_and_keeps_timed_sets_cold(nsets, warmup, steps):
+    """Set-up runs every buffer set once before anything is timed, and every
+    timed step's set was last used exactly nsets - 1 steps before it."""
+    o = bench.rotation(nsets, warmup, steps)
+    assert sorted(o["setup"]) == list(range(nsets))
+    seq = o["setup"] + o["warmup"] + o["headline"] + o["event"]
+    t0 = len(o["setup"]) + len(o["warmup"])
+    last = {}
+    for i, j in enumerate(seq):
+        if i >= t0:
+            assert j in last                          # never first touched in a timed phase
+            assert i - last[j] == nsets, (i, j, last[j])  # nsets - 1 other steps in between
+        last[j] = i

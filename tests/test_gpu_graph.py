@@ -2,12 +2,15 @@
 reproduce the eager results bit for bit.  Between replays the outputs are
 cleared and other library work runs eagerly, with synchronisations, so a
 replay that leans on state left by the previous one would show."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
 
 import workloads as W
 import combine_moe_layout_04_amd as M
+from combine_moe_layout_04_amd._lib import lib
 
 from devutil import to_dev
 
@@ -19,9 +22,11 @@ def say(msg):
     print(msg, flush=True)
 
 
-def make_step(cfg, inp, pad_multiple=1, staged=False):
+def make_step(cfg, inp, pad_multiple=1, staged=False, noalloc=False):
     """Device inputs, preallocated outputs, and a closure running one step
-    into them (no allocation inside, so it can be captured)."""
+    into them (no allocation inside, so it can be captured).  noalloc: the
+    layout is moe_layout_noalloc (its histogram in the library's static
+    per-device scratch), called through the C ABI."""
     dt = cfg.dtype
     h = M.Handle(pad_multiple=pad_multiple)
     idx = torch.from_numpy(inp.topk_idx).to(DEV)
@@ -42,8 +47,18 @@ def make_step(cfg, inp, pad_multiple=1, staged=False):
                grad_y=rows(R), grad_w=torch.zeros((cfg.T, cfg.K), dtype=torch.float32, device=DEV),
                grad_x=rows(cfg.T), S=rows(cap), Q=rows(cap))
 
+    def layout():
+        if not noalloc:
+            M.moe_layout(idx, cfg.E, cfg.P, handle=h, workspace=ws)
+            return
+        stream = torch.cuda.current_stream(DEV).cuda_stream
+        rc = lib().moe_layout_noalloc(h.ptr, ctypes.c_void_p(idx.data_ptr()), 0, cfg.T, cfg.K, cfg.E, cfg.P,
+                                      ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(stream))
+        assert rc == 0, rc
+        h.workspace, h.T, h.K, h.E, h.P, h.R, h.device = ws, cfg.T, cfg.K, cfg.E, cfg.P, R, DEV
+
     def step():
-        M.moe_layout(idx, cfg.E, cfg.P, handle=h, workspace=ws)
+        layout()
         if staged:
             M.moe_send(h, x, send=out["S"])
             M.moe_expand(h, out["S"], w, recv=out["recv"], recv_scores=out["scores"])
@@ -67,12 +82,16 @@ def same(a, b):
                        b.view(torch.uint8) if b.dtype != torch.uint8 else b)
 
 
-@pytest.mark.parametrize("pad_multiple,staged", [(1, False), (16, False), (1, True)])
-def test_step_replays_bitwise(pad_multiple, staged):
+@pytest.mark.parametrize("pad_multiple,staged,noalloc", [(1, False, False), (16, False, False), (1, True, False),
+                                                          (1, False, True), (16, True, True)])
+def test_step_replays_bitwise(pad_multiple, staged, noalloc):
+    """noalloc: the layout without a workspace histogram, the caller it is
+    for; the layer run between replays also uses it, so the static scratch
+    holds another layer's histogram when each replay starts."""
     cfg = W.get_config("qwen3_30b_a3b", T=1024)
-    say(f"graph pad={pad_multiple} staged={staged}")
+    say(f"graph pad={pad_multiple} staged={staged} noalloc={noalloc}")
     inp = W.layer_inputs(cfg, seed=11)
-    h, out, step = make_step(cfg, inp, pad_multiple, staged)
+    h, out, step = make_step(cfg, inp, pad_multiple, staged, noalloc)
     # eager reference
     step()
     torch.cuda.synchronize()
@@ -80,7 +99,7 @@ def test_step_replays_bitwise(pad_multiple, staged):
     ref = snapshot(out)
     # other work between replays: a second layer with its own handle
     other = W.layer_inputs(W.get_config("qwen3_30b_a3b", T=700), seed=12)
-    _, _, other_step = make_step(W.get_config("qwen3_30b_a3b", T=700), other)
+    _, _, other_step = make_step(W.get_config("qwen3_30b_a3b", T=700), other, noalloc=noalloc)
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
