@@ -70,7 +70,8 @@ def parse():
     ap.add_argument("--waves-per-block", type=int, default=0)
     ap.add_argument("--layout-pairs", type=int, default=0)
     ap.add_argument("--gather-mode", type=int, default=0,
-                    help="receive rows of the gathers: 0 in registers, 1 staged in LDS")
+                    help="receive rows of the gathers: 0 by row width (LDS-staged above 4 KiB), "
+                         "1 staged in LDS, 2 in registers")
     ap.add_argument("--events", choices=["kernel", "all", "none"], default="kernel",
                     help="HIP events of the event pass, which repeats the timed steps after the "
                          "headline loop (the headline loop itself records no event). kernel: the "

@@ -203,7 +203,7 @@ int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pa
     if (n < 0 || n > 2) return MOE_ERR_INVALID_ARG;
     if (!(w == 0 || w == 1 || w == 2 || w == 4 || w == 8)) return MOE_ERR_INVALID_ARG;
     if (!(lp == 0 || lp == 512 || lp == 1024 || lp == 2048 || lp == 4096)) return MOE_ERR_INVALID_ARG;
-    if (tuning->gather_mode != 0 && tuning->gather_mode != 1) return MOE_ERR_INVALID_ARG;
+    if (tuning->gather_mode < 0 || tuning->gather_mode > 2) return MOE_ERR_INVALID_ARG;
     t.gather_mode = tuning->gather_mode;
     if (c) t.chunks_per_lane = c;
     t.nontemporal = n;

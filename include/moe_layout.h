@@ -108,7 +108,9 @@ typedef struct moe_tuning {
   int waves_per_block;  /* wavefronts per workgroup of the row kernels: 0 (= 4), 1, 2, 4, 8 */
   int layout_pairs;     /* (t,k) pairs per layout tile: 0 (= 512), 512, 1024, 2048, 4096      */
   int gather_mode;      /* receive rows of the gathers (moe_combine, unscaled moe_dispatch_bwd):
-                           0 (default) in registers; 1 staged in LDS by direct loads        */
+                           0 (default) by row width: staged in LDS by direct loads for rows
+                           wider than 4 KiB, in registers otherwise; 1 always LDS-staged;
+                           2 always in registers                                         */
 } moe_tuning;
 
 typedef struct moe_handle_s* moe_handle_t;

@@ -121,7 +121,7 @@ def test_handle_lifecycle_and_tuning(L):
     assert L.moe_handle_destroy(None) == C["MOE_ERR_INVALID_ARG"]
     assert L.moe_handle_create(None, None) == C["MOE_ERR_INVALID_ARG"]
     for bad in (MoeTuning(3, 0, 0, 0), MoeTuning(0, 3, 0, 0), MoeTuning(0, 0, 3, 0),
-                MoeTuning(0, 0, 0, 300), MoeTuning(0, 0, 0, 8192), MoeTuning(0, 0, 0, 0, 2),
+                MoeTuning(0, 0, 0, 300), MoeTuning(0, 0, 0, 8192), MoeTuning(0, 0, 0, 0, 3),
                 MoeTuning(0, 0, 0, 0, -1)):
         assert L.moe_handle_create(ctypes.byref(h), ctypes.byref(bad)) == C["MOE_ERR_INVALID_ARG"]
     good = MoeTuning(2, 2, 8, 2048, 1)

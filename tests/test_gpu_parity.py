@@ -345,7 +345,8 @@ RAGGED = [  # name, overrides
                                     dict(chunks_per_lane=4, nontemporal=1, waves_per_block=2,
                                          layout_pairs=4096),
                                     dict(gather_mode=1),
-                                    dict(gather_mode=1, nontemporal=0, waves_per_block=8)])
+                                    dict(gather_mode=1, nontemporal=0, waves_per_block=8),
+                                    dict(gather_mode=2, waves_per_block=2)])
 def test_layer_ragged_rows_all_tunings(name, over, tuning):
     cfg = W.get_config(name, **over)
     say(f"ragged {name} {over} {tuning}")
@@ -369,11 +370,13 @@ def test_lds_staged_gather_full_size(name):
     w = None if cfg.absorbed else torch.from_numpy(inp.topk_weights).to(DEV)
     y, gr = (to_dev(a, dt, DEV) for a in (inp.y, inp.grad_recv))
     outs = {}
-    for mode in (0, 1):
+    for mode in (2, 1, 0):   # registers, LDS-staged, by row width (the default)
         h = M.moe_layout(idx, cfg.E, cfg.P, handle=M.Handle(gather_mode=mode))
         outs[mode] = (M.moe_combine(h, y, w), M.moe_dispatch_bwd(h, gr)[0])
         assert h.check() == 0
-    for a, b in zip(outs[0], outs[1]):
+    for a, b, c in zip(outs[2], outs[1], outs[0]):
+        assert torch.equal(a.view(torch.int16 if dt == "bf16" else torch.int32),
+                           c.view(torch.int16 if dt == "bf16" else torch.int32))
         assert torch.equal(a.view(torch.int16 if dt == "bf16" else torch.int32),
                            b.view(torch.int16 if dt == "bf16" else torch.int32))
     lay = O.layout(inp.topk_idx, cfg.E, cfg.P)
