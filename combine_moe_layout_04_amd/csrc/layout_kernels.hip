@@ -15,15 +15,19 @@
 //          flight), then one workgroup scan over the columns: every global
 //          offset and this tile's starts.  Token send slots come from
 //          per-partition ballots over the tile's tokens (with send_token,
-//          their inverse).  The tile's ids are
-//          staged in LDS; each wave ranks a contiguous span of pairs: wave64
-//          ballots match equal ids, a popcount over the lanes below gives
-//          the rank inside 64 pairs, and per-(wave, expert) cursors in LDS
-//          carry it across waves (and rounds).  No position is ever taken
-//          from an atomic, so the result depends on the routing alone (an
-//          activation-checkpoint replay of the same routing reproduces it
-//          bit for bit).  Global stores come after the last workgroup
-//          barrier: a barrier waits for the workgroup's outstanding stores.
+//          their inverse).  Each wave ranks a contiguous span of pairs:
+//          wave64 ballots match equal ids, a popcount over the lanes below
+//          gives the rank inside 64 pairs, and per-(wave, expert) first rows
+//          place the waves.  No position is ever taken from an atomic, so
+//          the result depends on the routing alone (an activation-checkpoint
+//          replay of the same routing reproduces it bit for bit).  Global
+//          stores come after the last workgroup barrier: a barrier waits for
+//          the workgroup's outstanding memory operations.
+//          Two forms: layout_rank_wave_kernel for the usual tile (at most 512
+//          pairs, one per thread, so each wave holds one span of 64, and at
+//          most 512 columns), with three workgroup barriers; and
+//          layout_rank_kernel for larger tiles, which stages the ids in LDS
+//          and carries per-(wave, expert) cursors across rounds.
 //
 // Ids outside [0,E) go to an extra bucket E, sorted after every expert, so
 // that every position stays inside [0, T*K) even for bad input; the rank

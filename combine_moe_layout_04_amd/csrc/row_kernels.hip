@@ -17,9 +17,10 @@
 //   gather (receive rows -> token): forward combine, and the backward of an
 //     unscaled dispatch.  One wave loads its segment of up to 8 receive rows
 //     (non-temporal: read once), sums them in float32 in k order from +0.0
-//     (product and sum rounded separately) and rounds once.  The compiled
-//     code issues the 8 loads one after another; issuing them together
-//     measured no faster, since the resident waves already keep HBM busy.
+//     (product and sum rounded separately) and rounds once.  For rows wider
+//     than 4 KiB the rows are staged in LDS by direct loads instead
+//     (gather_lds_kernel, the same sums), which measured 2.4-2.7 us faster
+//     per launch there; at 4 KiB rows the two are level.
 //   token dot (one workgroup per token, one wave per segment): the
 //     router-weight gradients <tok[t], rcv[recv_pos[t,k]]>, in the fixed
 //     order of moe_layout.h: per-chunk partials in element order, a butterfly
