@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--waves-per-block", type=int, default=0)
     ap.add_argument("--layout-pairs", type=int, default=0)
     ap.add_argument("--gather-mode", type=int, default=0,
-                    help="receive rows of the gathers: 0 by row width (LDS-staged above 4 KiB), "
+                    help="receive rows of the gathers: 0 by row width (LDS-staged from 4 KiB), "
                          "1 staged in LDS, 2 in registers")
     ap.add_argument("--events", choices=["kernel", "all", "none"], default="kernel",
                     help="HIP events of the event pass, which repeats the timed steps after the "
@@ -203,11 +203,10 @@ def index_bytes(cfg, staged=False, n_send=None, pad_rows=None):
     return sum(per[kind] for _, kind, _, _ in step_calls(cfg, staged, n_send, pad_rows))
 
 
-# The call whose kernel the roofline reports: the K-row gather-reduce (in the
-# staged exchange, its receiver-side half).
-# The call whose kernel is the step's longest launch, measured cold: the
-# dispatch's row scatter on every direct shape (Qwen3-30B-A3B 29.0 us against
-# 27.3 for the combine's gather; DeepSeek-V3 110.0 against 97.2; the
+# The call whose kernel the roofline reports, the step's longest launch
+# measured cold: the dispatch's row scatter on every direct shape
+# (Qwen3-30B-A3B 29.0 us against 27.3 for the combine's gather; DeepSeek-V3
+# 110.0 against 97.2; the
 # DiffusionGemma scaled dispatch 78.6 us, five times a step), and on the
 # staged path the dispatch's expansion (39.5 us, beside the combine
 # backward's scaled expansion at 40.6 and the partition reduce at 37.4).

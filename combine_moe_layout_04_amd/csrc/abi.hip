@@ -191,11 +191,12 @@ int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pa
   if (!out) return MOE_ERR_INVALID_ARG;
   if (pad_multiple < 1 || pad_multiple > moe::kMaxPadMultiple) return MOE_ERR_INVALID_ARG;
   // defaults: one segment per wave, non-temporal receive rows and token-row
-  // stores, 4 waves per workgroup, 512-pair layout tiles.  Measured on the
+  // stores, 4 waves per workgroup (the LDS-staged gather: 1 at rows of whole
+  // segments not a multiple of 8 in number), 512-pair layout tiles.  Measured on the
   // Qwen3-shaped layer (one box, interleaved runs): non-temporal token-row
   // stores take the step from 149.3 to 145.8 us; two segments per wave then
   // gain nothing in the gathers and cost 3 us in each scatter.
-  moe::Tuning t{1, 2, 4, moe::kLayoutThreads, 0};
+  moe::Tuning t{1, 2, 4, moe::kLayoutThreads, 0, 0};
   if (tuning) {
     const int c = tuning->chunks_per_lane, n = tuning->nontemporal, w = tuning->waves_per_block;
     const int lp = tuning->layout_pairs;
@@ -207,7 +208,7 @@ int moe_handle_create_padded(moe_handle_t* out, const moe_tuning* tuning, int pa
     t.gather_mode = tuning->gather_mode;
     if (c) t.chunks_per_lane = c;
     t.nontemporal = n;
-    if (w) t.waves_per_block = w;
+    if (w) t.waves_per_block = t.gather_waves = w;
     if (lp) t.layout_pairs = lp;
   }
   moe_handle_s* h = new (std::nothrow) moe_handle_s();

@@ -154,7 +154,10 @@ struct Tuning {
   int nontemporal;      // 0, 1, 2
   int waves_per_block;  // 1, 2, 4, 8
   int layout_pairs;     // 512, 1024, 2048, 4096
-  int gather_mode;      // 0: by row width (LDS-staged above 4 KiB); 1: LDS-staged (gather_lds_kernel); 2: registers
+  int gather_mode;      // 0: by row width (LDS-staged from 4 KiB); 1: LDS-staged (gather_lds_kernel);
+                        // 2: registers (gather_kernel)
+  int gather_waves;     // waves per workgroup of the LDS-staged gather: waves_per_block when
+                        // that is set, else 0 (by row width, lds_gather_waves)
   // measurement: when ev_stop is set, the launch goes through
   // hipExtLaunchKernel, which binds ev_stop to the kernel's completion and,
   // when ev_start is set too, records ev_start just before the kernel; null

@@ -17,10 +17,10 @@
 //   gather (receive rows -> token): forward combine, and the backward of an
 //     unscaled dispatch.  One wave loads its segment of up to 8 receive rows
 //     (non-temporal: read once), sums them in float32 in k order from +0.0
-//     (product and sum rounded separately) and rounds once.  For rows wider
-//     than 4 KiB the rows are staged in LDS by direct loads instead
-//     (gather_lds_kernel, the same sums), which measured 2.4-2.7 us faster
-//     per launch there; at 4 KiB rows the two are level.
+//     (product and sum rounded separately) and rounds once.  For rows of
+//     4 KiB and wider the rows are staged in LDS by direct loads instead
+//     (gather_lds_kernel, the same sums), which measured 0.3-3 us faster per
+//     launch there.
 //   token dot (one workgroup per token, one wave per segment): the
 //     router-weight gradients <tok[t], rcv[recv_pos[t,k]]>, in the fixed
 //     order of moe_layout.h: per-chunk partials in element order, a butterfly
@@ -431,11 +431,28 @@ hipError_t ga_mode(const GatherArgs& a, const Tuning& t, hipStream_t s) {
   return a.w ? go_gather<DT, CPL, true>(a, t, s) : go_gather<DT, CPL, false>(a, t, s);
 }
 
+// Waves per workgroup of the LDS-staged gather when the handle leaves it
+// open.  Workgroups are dealt to the eight XCDs in turn, so with one wave per
+// workgroup the segments of a token row spread over several XCDs.  Measured
+// per launch (kernel trace, bfloat16, T = 4096 and 8192, rows of 4 to 14 KiB,
+// 1, 2 and 4 waves per workgroup): one wave was the fastest, by 0.1-3.3 us,
+// at every width whose segments are all full, except rows of 8 segments,
+// where the deal gives XCD x segment x of every row and one wave ran 8 us
+// (T = 4096) and 3 us (T = 8192) slower than two or four.  At 5.5 KiB rows
+// (a half segment last) the plain sum ran 1.3 us slower with one wave at
+// T = 8192.  So one wave for rows of whole segments whose count is not a
+// multiple of 8, else the handle's waves_per_block.  Renumbering the
+// workgroups so that each XCD takes one contiguous run of tokens measured
+// 3-11% slower at every width, for both gathers and the scatter.
+int lds_gather_waves(int NV, int ngrp, int waves_per_block) {
+  return (NV % kWave == 0 && ngrp % 8 != 0) ? 1 : waves_per_block;
+}
+
 template <int DT, bool W>
 hipError_t go_gather_lds(const GatherArgs& a0, const Tuning& tu, hipStream_t s) {
   GatherArgs a = a0;
   a.ngrp = groups_per_token(a.NV, 1);
-  const int wpb = tu.waves_per_block;
+  const int wpb = tu.gather_waves ? tu.gather_waves : lds_gather_waves(a.NV, a.ngrp, tu.waves_per_block);
   const int64_t waves = (int64_t)a.T * a.ngrp;
   const dim3 grid((unsigned)((waves + wpb - 1) / wpb)), block(wpb * kWave);
   const uint32_t lds = (uint32_t)(wpb * KG * kWave * sizeof(u32x4));
@@ -447,16 +464,18 @@ hipError_t go_gather_lds(const GatherArgs& a0, const Tuning& tu, hipStream_t s) 
   return hipGetLastError();
 }
 
-// Which gather reads the receive rows.  By default the LDS-staged one for rows
-// wider than 4 KiB (more than 256 chunks) and the register one otherwise.
-// Measured per launch (kernel trace, register vs LDS-staged): DeepSeek-V3
-// rows of 14 KiB, combine 94.63 vs 91.95 us and dispatch backward 92.61 vs
-// 90.19; DiffusionGemma rows of 5.5 KiB, combine 71.27 vs 68.89; Qwen3-30B-A3B
-// rows of 4 KiB, 27.52 vs 27.60 and 26.58 vs 26.78.
+// Which gather reads the receive rows.  By default the LDS-staged one for
+// rows of 4 KiB (256 chunks) and wider, the register one below.  Measured per
+// launch (kernel trace, bfloat16, register gather at 4 waves per workgroup
+// against the LDS-staged one at lds_gather_waves): Qwen3-30B-A3B rows of
+// 4 KiB, combine 27.52 vs 26.64 us and dispatch backward 26.58 vs 26.28;
+// DeepSeek-V3 rows of 14 KiB, 94.63 vs 91.65 and 92.61 vs 90.47;
+// DiffusionGemma rows of 5.5 KiB, plain combine 71.27 vs 69.11.  Narrower
+// rows were not measured.
 bool gather_in_lds(const GatherArgs& a, const Tuning& t) {
   if (t.gather_mode == 1) return true;
   if (t.gather_mode == 2) return false;
-  return a.NV > 256;
+  return a.NV >= 256;
 }
 
 template <int DT>

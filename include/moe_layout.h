@@ -105,11 +105,13 @@ typedef struct moe_tuning {
                            lane keeps in flight: 0 (= 1), 1, 2 or 4                        */
   int nontemporal;      /* 0: default loads/stores; 1: receive-row loads and stores
                            marked non-temporal; 2 (default): token-row stores too    */
-  int waves_per_block;  /* wavefronts per workgroup of the row kernels: 0 (= 4), 1, 2, 4, 8 */
+  int waves_per_block;  /* wavefronts per workgroup of the row kernels: 0 (= 4; the
+                           LDS-staged gather takes 1 when a row is whole segments and
+                           their number is not a multiple of 8), 1, 2, 4, 8              */
   int layout_pairs;     /* (t,k) pairs per layout tile: 0 (= 512), 512, 1024, 2048, 4096      */
   int gather_mode;      /* receive rows of the gathers (moe_combine, unscaled moe_dispatch_bwd):
                            0 (default) by row width: staged in LDS by direct loads for rows
-                           wider than 4 KiB, in registers otherwise; 1 always LDS-staged;
+                           of 4 KiB and wider, in registers otherwise; 1 always LDS-staged;
                            2 always in registers                                         */
 } moe_tuning;
 

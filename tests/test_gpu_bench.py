@@ -23,7 +23,7 @@ def run_bench(*extra):
 
 
 @pytest.mark.parametrize("extra", [(), ("--staged",), ("--pad-multiple", "16"), ("--graph",),
-                                   ("--events", "all"), ("--gather-mode", "1"), ("--warm",)])
+                                   ("--events", "all"), ("--gather-mode", "2"), ("--warm",)])
 def test_bench_line(extra):
     d = run_bench(*extra)
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",

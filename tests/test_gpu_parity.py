@@ -335,6 +335,8 @@ RAGGED = [  # name, overrides
     ("diffusion_gemma", dict(T=67, H=520)),
     ("deepseek_v3", dict(T=45, H=4104)),
     ("deepseek_v3", dict(T=19, H=8712)),    # 18 segments: more than one per dot wave
+    ("qwen3_30b_a3b", dict(T=77, H=4096)),  # 8 segments: the LDS gather keeps 4 waves per workgroup
+    ("deepseek_v3", dict(T=23, H=8192)),    # 16 segments
 ]
 
 
@@ -344,7 +346,7 @@ RAGGED = [  # name, overrides
                                          layout_pairs=2048),
                                     dict(chunks_per_lane=4, nontemporal=1, waves_per_block=2,
                                          layout_pairs=4096),
-                                    dict(gather_mode=1),
+                                    dict(gather_mode=2),
                                     dict(gather_mode=1, nontemporal=0, waves_per_block=8),
                                     dict(gather_mode=2, waves_per_block=2)])
 def test_layer_ragged_rows_all_tunings(name, over, tuning):
@@ -356,13 +358,15 @@ def test_layer_ragged_rows_all_tunings(name, over, tuning):
     compare_layer(cfg, res, ref)
 
 
-@pytest.mark.parametrize("name", list(W.CONFIGS))
+@pytest.mark.parametrize("name", list(W.CONFIGS) + ["qwen3_30b_a3b:H=4096"])
 def test_lds_staged_gather_full_size(name):
     """The LDS-staged gather (receive rows loaded straight into LDS) gives the
     register gather's sums bit for bit, on every full-size layer, for the
     combine (weighted or plain) and the unscaled dispatch backward; the
-    combine is also checked against the oracle."""
-    cfg = W.get_config(name)
+    combine is also checked against the oracle.  The last case has rows of
+    8 segments, where the LDS gather keeps 4 waves per workgroup."""
+    base, _, h_over = name.partition(":H=")
+    cfg = W.get_config(base, **({"H": int(h_over)} if h_over else {}))
     dt = cfg.dtype
     say(f"lds gather {name} T={cfg.T} H={cfg.H} {dt} K={cfg.K}")
     inp = W.layer_inputs(cfg, seed=8)
