@@ -97,7 +97,10 @@ def parse():
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the 1 GiB copy that measures the achievable HBM ceiling")
     ap.add_argument("--graph", action="store_true",
-                    help="replay each step as a captured HIP graph (no per-call events)")
+                    help="replay the steps as captured HIP graphs (no per-call events)")
+    ap.add_argument("--graph-steps", type=int, default=1,
+                    help="with --graph, consecutive steps of the rotation per captured graph (a divisor "
+                         "of --steps and --warmup)")
     return ap.parse_args()
 
 
@@ -536,6 +539,10 @@ def main():
         print(f"bench.py measures one GPU's share of the exchange; --gpus {args.gpus} is not "
               "supported (this path has no collectives and runs on one GPU).", file=sys.stderr)
         sys.exit(2)
+    G = args.graph_steps
+    if G < 1 or (G > 1 and (not args.graph or args.steps % G or args.warmup % G)):
+        print("--graph-steps needs --graph and must divide --steps and --warmup", file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -745,29 +752,31 @@ def main():
                 step(s)  # warm the capture stream
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        for s in sets:
+        for j in range(nsets):  # graph j: the G steps of the rotation from set j on
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(s)
+                for u in range(G):
+                    step(sets[(j + u) % nsets])
             graphs.append(g)
         for g in graphs:
             g.replay()
-        for i in range(args.warmup):
+        for i in range(0, args.warmup, G):
             graphs[i % nsets].replay()
         torch.cuda.synchronize()
     eager = graphs is None
 
     def run_steps(K, start, ev=None):
         # steps start .. start+K-1 of the rotation
-        for i in range(K):
-            if not eager:
+        if not eager:  # one replay runs G steps
+            for i in range(0, K, G):
                 if ev is not None:
-                    ev["sev"].record(i, stream)
+                    ev["sev"].record(i // G, stream)
                 graphs[(first + start + i) % nsets].replay()
-            else:
-                step(set_of(start + i), ev, i)
-        if not eager and ev is not None:
-            ev["sev"].record(K, stream)
+            if ev is not None:
+                ev["sev"].record(K // G, stream)
+            return
+        for i in range(K):
+            step(set_of(start + i), ev, i)
 
     # The headline: K steps of plain launches (or graph replays), bracketed
     # by synchronisations, wall clock only.  No event is recorded or bound
@@ -804,7 +813,7 @@ def main():
         ev["hev"] = HipEvents(ev["per_step"] * K)
         ev["kev"] = HipEvents(2 * len(ksteps))
         ev["bev"] = HipEvents(K) if eager else None
-        ev["sev"] = HipEvents(K + 1 if not eager else 0)
+        ev["sev"] = HipEvents(K // G + 1 if not eager else 0)
         torch.cuda.synchronize()
         e0 = time.perf_counter()
         run_steps(K, K, ev)  # the rotation continues where the headline left it
@@ -816,8 +825,8 @@ def main():
         if eager and K > 1:   # end of step i-1's last kernel to end of step i's
             clean = [i for i in range(1, K) if i not in ev["kslot"]] or list(range(1, K))
             st = np.array([ev["bev"].elapsed_ms(i - 1, i) for i in clean]) * 1e3
-        elif not eager:
-            st = np.array([ev["sev"].elapsed_ms(i, i + 1) for i in range(K)]) * 1e3
+        elif not eager:  # per replay, divided over its G steps
+            st = np.array([ev["sev"].elapsed_ms(i, i + 1) for i in range(K // G)]) * 1e3 / G
         for k in ("hev", "kev", "bev", "sev"):
             if ev[k] is not None:
                 ev[k].close()
@@ -915,7 +924,7 @@ def main():
             "event_pass_us_per_step": None if ev_ms_per_step is None else round(ev_ms_per_step * 1e3, 2),
             "step_us": step_us,
             **({} if per_pass is None else {"per_pass_us": per_pass}),
-            "timing": ("hip graph replays" if graphs is not None else "eager launches") +
+            "timing": (f"hip graph replays, {G} step(s) per graph" if graphs is not None else "eager launches") +
                       f"; headline loop without events, set-up touches all {nsets} sets first; event pass "
                       f"(same {K} steps): {events}" +
                       (f", dominant kernel timed on {len(ksteps)} of {K} steps" if ksteps else ""),

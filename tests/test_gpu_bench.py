@@ -23,7 +23,8 @@ def run_bench(*extra):
 
 
 @pytest.mark.parametrize("extra", [(), ("--staged",), ("--pad-multiple", "16"), ("--graph",),
-                                   ("--events", "all"), ("--gather-mode", "2"), ("--warm",)])
+                                   ("--graph", "--graph-steps", "2"), ("--events", "all"),
+                                   ("--gather-mode", "2"), ("--warm",)])
 def test_bench_line(extra):
     d = run_bench(*extra)
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
@@ -36,6 +37,9 @@ def test_bench_line(extra):
     assert abs(d["value"] - cfg["bytes_per_step"] / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"] + 0.01
     if "--graph" in extra:
         assert d["roofline"] is None          # kernel events are for eager launches
+        per_graph = extra[-1] if "--graph-steps" in extra else "1"
+        assert f"{per_graph} step(s) per graph" in cfg["timing"]
+        assert cfg["step_us"]["n"] == 4 // int(per_graph)
     else:
         r = d["roofline"]
         assert r["bound"] == "hbm" and r["peak"] == 8000.0 and 0 < r["frac"] < 1
