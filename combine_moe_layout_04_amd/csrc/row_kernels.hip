@@ -470,8 +470,8 @@ hipError_t go_gather_lds(const GatherArgs& a0, const Tuning& tu, hipStream_t s) 
 // against the LDS-staged one at lds_gather_waves): Qwen3-30B-A3B rows of
 // 4 KiB, combine 27.52 vs 26.64 us and dispatch backward 26.58 vs 26.28;
 // DeepSeek-V3 rows of 14 KiB, 94.63 vs 91.65 and 92.61 vs 90.47;
-// DiffusionGemma rows of 5.5 KiB, plain combine 71.27 vs 69.11.  Narrower
-// rows were not measured.
+// DiffusionGemma rows of 5.5 KiB, plain combine 71.27 vs 69.11.  At rows of
+// 0.5-3 KiB neither form was consistently faster over T = 4096-16384.
 bool gather_in_lds(const GatherArgs& a, const Tuning& t) {
   if (t.gather_mode == 1) return true;
   if (t.gather_mode == 2) return false;
