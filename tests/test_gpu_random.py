@@ -30,7 +30,10 @@ def draw_case(i):
     T = int(rng.choice([0, 1, 2, 7, 33, 64, 65, 130, 257]))
     dtype = str(rng.choice(["f32", "bf16"]))
     per_chunk = 4 if dtype == "f32" else 8
-    H = per_chunk * int(rng.choice([1, 3, 63, 64, 65, 130, 200]))
+    # chunks per row: up to 200 the register gather runs by default; from 256
+    # the LDS-staged one, at one wave per workgroup (256, 896: whole segments)
+    # or the row kernels' four (352: half a segment last; 512: 8 segments)
+    H = per_chunk * int(rng.choice([1, 3, 63, 64, 65, 130, 200, 256, 352, 512, 896]))
     pad = int(rng.choice([1, 1, 2, 5, 16]))
     absorbed = bool(rng.random() < 0.3)
     dup = bool(rng.random() < 0.25)
