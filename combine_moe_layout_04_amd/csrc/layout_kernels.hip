@@ -401,7 +401,6 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
       wpre[item] = s;
     }
     __syncthreads();
-#pragma unroll 4
     for (int r = 0; r < a.P; ++r) {  // uniform: every lane takes part in the ballot
       const int on = (int)((m >> r) & 1ull);
       const uint64_t bal = __ballot(on);

@@ -109,7 +109,6 @@ __global__ __launch_bounds__(512) void scatter_kernel(ScatterArgs a) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) unpack<DT>(v[c], f[c]);
   }
-#pragma unroll 4
   for (int k = 0; k < a.K; ++k) {
     const int p = read_lane_i(q.pos, k);
     if ((unsigned)p >= (unsigned)a.R) continue;  // uniform
