@@ -57,6 +57,16 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
+@pytest.mark.parametrize("extra", [("--graph-steps", "2"),                         # without --graph
+                                   ("--graph", "--graph-steps", "3"),              # 3 does not divide 200
+                                   ("--graph", "--graph-steps", "4", "--warmup", "6"),
+                                   ("--graph", "--graph-steps", "0")])
+def test_graph_steps_must_divide_the_run(extra):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *extra],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--graph-steps" in r.stderr and not r.stdout
+
+
 def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
     """The counters stay valid while the dominant kernel, its launcher and
     the device helpers are unchanged; an edit elsewhere in the file keeps
