@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     moe_dispatch,
     moe_dispatch_bwd,
     moe_layout,
+    moe_layout_noalloc,
     moe_workspace_size,
     moe_send_capacity,
     moe_recv_capacity,

@@ -160,6 +160,19 @@ class Handle:
 def moe_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
                handle: Optional[Handle] = None, workspace: Optional[torch.Tensor] = None) -> Handle:
     """Layout of one routing decision; returns the handle (see moe_layout.h)."""
+    return _layout("moe_layout", topk_idx, num_experts, num_partitions, handle, workspace)
+
+
+def moe_layout_noalloc(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
+                       handle: Optional[Handle] = None, workspace: Optional[torch.Tensor] = None) -> Handle:
+    """moe_layout whose histogram scratch is the library's static per-GPU array
+    (see moe_layout.h).  The library call allocates nothing; this wrapper
+    allocates only when it has to create the workspace, so a caller that passes
+    one, or reuses the handle's, allocates nothing at all (graph capture)."""
+    return _layout("moe_layout_noalloc", topk_idx, num_experts, num_partitions, handle, workspace)
+
+
+def _layout(entry, topk_idx, num_experts, num_partitions, handle, workspace) -> Handle:
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
     dev = topk_idx.device
@@ -181,8 +194,8 @@ def moe_layout(topk_idx: torch.Tensor, num_experts: int, num_partitions: int,
     else:
         _need(workspace, "workspace", dev, dtype=torch.uint8)
         ws = workspace  # the library checks its size
-    _check(lib().moe_layout(h.ptr, _ptr(topk_idx), itype, T, K, E, P, _ptr(ws), ws.numel(),
-                            _stream(dev)), "moe_layout")
+    _check(getattr(lib(), entry)(h.ptr, _ptr(topk_idx), itype, T, K, E, P, _ptr(ws), ws.numel(),
+                                 _stream(dev)), entry)
     if (h.T, h.K, h.E, h.P) != (T, K, E, P) or h.R is None:
         n = ctypes.c_int64(0)
         _check(lib().moe_recv_capacity(h.ptr, ctypes.byref(n)), "moe_recv_capacity")

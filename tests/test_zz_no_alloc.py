@@ -75,6 +75,31 @@ def test_noalloc_layout_matches_moe_layout(name, T2, pad):
         assert torch.equal(s1[:rows], s2[:rows])
 
 
+def test_python_binding_of_the_noalloc_layout():
+    """M.moe_layout_noalloc: the same handle as M.moe_layout, and, given a
+    workspace, no new tensor from torch's allocator on either call."""
+    cfg = W.get_config("qwen3_30b_a3b")
+    ws = torch.empty(M.moe_workspace_size(cfg.T, cfg.K, cfg.E, cfg.P), dtype=torch.uint8, device=DEV)
+    h = M.Handle()
+    for T, seed in ((cfg.T, 31), (1234, 32)):
+        say(f"python noalloc layout T={T}")
+        c = W.get_config("qwen3_30b_a3b", T=T)
+        idx = torch.from_numpy(W.layer_inputs(c, seed=seed, with_rows=False).topk_idx).to(DEV)
+        ref = M.moe_layout(idx, c.E, c.P)
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated(DEV)
+        M.moe_layout_noalloc(idx, c.E, c.P, handle=h, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.cuda.memory_allocated(DEV) == before
+        n_send = int(ref.field("send_offset")[-1].item())
+        for f in FIELDS:
+            a, b = h.field(f), ref.field(f)
+            if f == "send_token":
+                a, b = a[:n_send], b[:n_send]
+            assert torch.equal(a, b), f
+        assert h.check() == 0 and h.R == ref.R
+
+
 def test_noalloc_layout_rejects_what_it_cannot_hold():
     """A shape whose histogram exceeds the static scratch is refused on the
     host (MOE_ERR_SCRATCH), and a short workspace with MOE_ERR_WORKSPACE."""
