@@ -1,0 +1,114 @@
+"""Receive buffers past 4 GiB: every row offset is 64-bit.
+
+A whole layer at T = 32768, K = 8, H = 8256 bf16 puts 262144 receive rows of
+16512 bytes in each receive buffer, 4.33 GB, so the last expert segments lie
+past byte 2^32 (and a row is 16.1 segments: a partial last segment).  The
+layout is compared with the oracle in full.  The rows are compared on a
+sample of tokens: every token with a row past 4 GiB (up to 512 of them,
+always including the owners of the first such row and of the last row), the
+first and last token and 64 random ones.  For the sample the oracle runs on
+the sub-problem of those tokens alone (their ids and weights, and the rows
+they read), whose results per token and per pair are the full problem's.
+Inputs are drawn on the device by torch's seeded generator; none comes from
+the library.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import combine_moe_layout_04_amd as M
+from oracle import moe_oracle as O
+from devutil import to_host
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+DT = "bf16"
+LAYOUT_FIELDS = ["num_tokens_per_expert", "num_tokens_per_rank", "expert_offset", "rank_offset",
+                 "send_offset", "recv_pos", "recv_token", "recv_k"]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def device_rows(n, H, seed):
+    """n x H bf16 rows of N(0,1) draws, made on the device in slices (no
+    full-size float32 temporary)."""
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    out = torch.empty((n, H), dtype=torch.bfloat16, device=DEV)
+    step = 1 << 15
+    for i in range(0, n, step):
+        m = min(step, n - i)
+        out[i:i + m] = torch.randn((m, H), generator=gen, device=DEV).to(torch.bfloat16)
+    return out
+
+
+def host_rows(t, rows):
+    """Rows of a device tensor, in the order given, as host bf16 bits."""
+    ix = torch.from_numpy(np.asarray(rows, np.int64).reshape(-1)).to(DEV)
+    return to_host(t.index_select(0, ix), DT)
+
+
+@pytest.mark.parametrize("absorbed", [False, True])
+def test_rows_past_4_gib(absorbed):
+    cfg = W.get_config("qwen3_30b_a3b").with_(T=32768, H=8256, absorbed=absorbed, renormalize=not absorbed)
+    T, H, K, E, P = cfg.T, cfg.H, cfg.K, cfg.E, cfg.P
+    R, row_bytes = T * K, H * 2
+    first_high = -(-(1 << 32) // row_bytes)   # first row whose byte offset is >= 2^32
+    assert R > first_high
+    say(f"rows past 4 GiB: T={T} H={H} bf16, {R} receive rows of {row_bytes} B, absorbed={absorbed}")
+
+    idx_np, w_np = W.routing(cfg, seed=61)
+    lay = O.layout(idx_np, E, P)
+    idx = torch.from_numpy(idx_np).to(DEV)
+    w = torch.from_numpy(w_np).to(DEV)
+    x = device_rows(T, H, 1)
+    g = device_rows(T, H, 2)
+    y = device_rows(R, H, 3)            # expert outputs; also the receive-row gradient below
+
+    h = M.moe_layout(idx, E, P)
+    for f in LAYOUT_FIELDS:
+        assert np.array_equal(h.field(f).cpu().numpy(), np.asarray(getattr(lay, f))), f
+    if absorbed:
+        recv, sc = M.moe_dispatch(h, x, w, scale_rows=True, recv_scores=True)
+        out = M.moe_combine(h, y)
+        gy, gw = M.moe_combine_bwd(h, g)
+        gx, gs = M.moe_dispatch_bwd(h, y, w, x, grad_s=True)
+    else:
+        recv, sc = M.moe_dispatch(h, x, w, recv_scores=True)
+        out = M.moe_combine(h, y, w)
+        gy, gw = M.moe_combine_bwd(h, g, w, y, grad_w=True)
+        gx, gs = M.moe_dispatch_bwd(h, y)
+    torch.cuda.synchronize()
+    assert h.check() == 0
+
+    rng = np.random.default_rng(7)
+    high = np.nonzero((lay.recv_pos >= first_high).any(axis=1))[0]
+    must = [int(lay.recv_token[first_high]), int(lay.recv_token[R - 1]), 0, T - 1]
+    pick = rng.choice(high, min(512, len(high)), replace=False)
+    S = np.unique(np.concatenate([must, pick, rng.choice(T, 64, replace=False)])).astype(np.int64)
+    say(f"{len(high)} tokens own rows past 4 GiB; {len(S)} tokens sampled")
+    pos = lay.recv_pos[S]                   # [n, K] rows in the full problem
+    sub = O.layout(idx_np[S], E, P)         # the sampled tokens alone
+    spos = sub.recv_pos.reshape(-1)         # their rows in the sub-problem, in (token, k) order
+    n = len(S)
+    x_s, g_s = host_rows(x, S), host_rows(g, S)
+    y_s = np.zeros((n * K, H), np.uint16)
+    y_s[spos] = host_rows(y, pos)
+    w_s = w_np[S]
+
+    r_recv, r_sc = O.dispatch(sub, x_s, DT, w_s, scale_rows=absorbed)
+    assert np.array_equal(host_rows(recv, pos), r_recv[spos]), "dispatch rows"
+    assert np.array_equal(sc.cpu().numpy()[pos.reshape(-1)], r_sc[spos]), "receive scores"
+    r_out = O.combine(sub, y_s, DT, None if absorbed else w_s)
+    assert np.array_equal(host_rows(out, S), r_out), "combine"
+    r_gy, r_gw = O.combine_bwd(sub, g_s, DT, None if absorbed else w_s, None if absorbed else y_s)
+    assert np.array_equal(host_rows(gy, pos), r_gy[spos]), "combine_bwd rows"
+    if not absorbed:
+        assert np.array_equal(gw.cpu().numpy()[S], r_gw), "grad_w"
+    r_gx, r_gs = O.dispatch_bwd(sub, y_s, DT, w_s if absorbed else None, x_s if absorbed else None)
+    assert np.array_equal(host_rows(gx, S), r_gx), "dispatch_bwd rows"
+    if absorbed:
+        assert np.array_equal(gs.cpu().numpy()[S], r_gs), "grad_s"
