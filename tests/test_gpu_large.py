@@ -112,3 +112,67 @@ def test_rows_past_4_gib(absorbed):
     assert np.array_equal(host_rows(gx, S), r_gx), "dispatch_bwd rows"
     if absorbed:
         assert np.array_equal(gs.cpu().numpy()[S], r_gs), "grad_s"
+
+
+@pytest.mark.parametrize("absorbed", [False, True])
+def test_staged_rows_past_4_gib(absorbed):
+    """The staged exchange with 32 KiB rows (H = 16384 bf16) at T = 32768: the
+    send buffer's used rows, the partials and the receive rows all run past
+    byte 2^32.  Send and partial rows are matched by (token, partition)
+    through each problem's own send_offset and token_slot."""
+    cfg = W.get_config("qwen3_30b_a3b").with_(T=32768, H=16384, absorbed=absorbed, renormalize=not absorbed)
+    T, H, K, E, P = cfg.T, cfg.H, cfg.K, cfg.E, cfg.P
+    R, row_bytes = T * K, H * 2
+    first_high = -(-(1 << 32) // row_bytes)
+    idx_np, w_np = W.routing(cfg, seed=62)
+    lay = O.layout(idx_np, E, P)
+    n_send = int(lay.send_offset[P])
+    assert n_send > first_high and R > first_high
+    say(f"staged rows past 4 GiB: T={T} H={H} bf16, {n_send} send rows, {R} receive rows of {row_bytes} B, "
+        f"absorbed={absorbed}")
+    idx = torch.from_numpy(idx_np).to(DEV)
+    w = torch.from_numpy(w_np).to(DEV)
+    x = device_rows(T, H, 11)
+    y = device_rows(R, H, 13)
+
+    h = M.moe_layout(idx, E, P)
+    for f in LAYOUT_FIELDS + ["token_slot"]:
+        assert np.array_equal(h.field(f).cpu().numpy(), np.asarray(getattr(lay, f))), f
+    send = M.moe_send(h, x)
+    recv, sc = M.moe_expand(h, send, w, scale_rows=absorbed, recv_scores=True)
+    partial = M.moe_reduce_partitions(h, y, None if absorbed else w)
+    out = M.moe_combine_partitions(h, partial)
+    torch.cuda.synchronize()
+    assert h.check() == 0
+
+    rng = np.random.default_rng(8)
+    srow_all = lay.send_offset[:P][None, :] + lay.token_slot      # send row of (t, r) where token_slot >= 0
+    high = np.nonzero(((lay.recv_pos >= first_high).any(axis=1))
+                      | ((lay.token_slot >= 0) & (srow_all >= first_high)).any(axis=1))[0]
+    must = [int(lay.recv_token[R - 1]), 0, T - 1]
+    S = np.unique(np.concatenate([must, rng.choice(high, min(512, len(high)), replace=False),
+                                  rng.choice(T, 64, replace=False)])).astype(np.int64)
+    say(f"{len(high)} tokens own rows past 4 GiB; {len(S)} tokens sampled")
+    sub = O.layout(idx_np[S], E, P)
+    on = lay.token_slot[S] >= 0                                     # [n, P], the same in both problems
+    assert np.array_equal(on, sub.token_slot >= 0)
+    full_send = (lay.send_offset[:P][None, :] + lay.token_slot[S])[on]
+    sub_send = (sub.send_offset[:P][None, :] + sub.token_slot)[on]
+    assert (full_send >= first_high).any()
+    pos = lay.recv_pos[S]
+    spos = sub.recv_pos.reshape(-1)
+    n = len(S)
+    x_s = host_rows(x, S)
+    y_s = np.zeros((n * K, H), np.uint16)
+    y_s[spos] = host_rows(y, pos)
+    w_s = w_np[S]
+
+    r_send = O.send(sub, x_s)
+    assert np.array_equal(host_rows(send, full_send), r_send[sub_send]), "send rows"
+    r_recv, r_sc = O.expand(sub, r_send, DT, w_s, scale_rows=absorbed)
+    assert np.array_equal(host_rows(recv, pos), r_recv[spos]), "expanded rows"
+    assert np.array_equal(sc.cpu().numpy()[pos.reshape(-1)], r_sc[spos]), "receive scores"
+    r_part = O.reduce_partitions(sub, y_s, DT, None if absorbed else w_s)
+    assert np.array_equal(host_rows(partial, full_send), r_part[sub_send]), "partials"
+    r_out = O.combine_partitions(sub, r_part, DT)
+    assert np.array_equal(host_rows(out, S), r_out), "merged rows"
