@@ -51,24 +51,25 @@ def host_rows(t, rows):
     return to_host(t.index_select(0, ix), DT)
 
 
-@pytest.mark.parametrize("absorbed", [False, True])
-def test_rows_past_4_gib(absorbed):
+@pytest.mark.parametrize("absorbed,pad", [(False, 1), (True, 1), (False, 128)])
+def test_rows_past_4_gib(absorbed, pad):
     cfg = W.get_config("qwen3_30b_a3b").with_(T=32768, H=8256, absorbed=absorbed, renormalize=not absorbed)
     T, H, K, E, P = cfg.T, cfg.H, cfg.K, cfg.E, cfg.P
-    R, row_bytes = T * K, H * 2
+    row_bytes = H * 2
     first_high = -(-(1 << 32) // row_bytes)   # first row whose byte offset is >= 2^32
-    assert R > first_high
-    say(f"rows past 4 GiB: T={T} H={H} bf16, {R} receive rows of {row_bytes} B, absorbed={absorbed}")
-
     idx_np, w_np = W.routing(cfg, seed=61)
-    lay = O.layout(idx_np, E, P)
+    lay = O.layout(idx_np, E, P, pad_multiple=pad)
+    R = len(lay.recv_token)                 # receive rows, padding included
+    assert R > first_high
+    say(f"rows past 4 GiB: T={T} H={H} bf16, {R} receive rows of {row_bytes} B, absorbed={absorbed} pad={pad}")
     idx = torch.from_numpy(idx_np).to(DEV)
     w = torch.from_numpy(w_np).to(DEV)
     x = device_rows(T, H, 1)
     g = device_rows(T, H, 2)
     y = device_rows(R, H, 3)            # expert outputs; also the receive-row gradient below
 
-    h = M.moe_layout(idx, E, P)
+    h = M.moe_layout(idx, E, P, handle=M.Handle(pad_multiple=pad))
+    assert M.moe_recv_capacity(h) == R
     for f in LAYOUT_FIELDS:
         assert np.array_equal(h.field(f).cpu().numpy(), np.asarray(getattr(lay, f))), f
     if absorbed:
@@ -83,19 +84,29 @@ def test_rows_past_4_gib(absorbed):
         gx, gs = M.moe_dispatch_bwd(h, y)
     torch.cuda.synchronize()
     assert h.check() == 0
+    if pad > 1:  # the padding rows of the segments past 4 GiB hold zeros (and zero scores)
+        eo = lay.expert_offset
+        fill = np.concatenate([np.arange(eo[e] + lay.num_tokens_per_expert[e], eo[e + 1]) for e in range(E)
+                               if eo[e + 1] > first_high])
+        fill = fill[fill >= first_high]
+        assert len(fill) > 0
+        for t in (recv, gy):
+            assert not host_rows(t, fill).any()
+        assert not sc.cpu().numpy()[fill].any()
 
     rng = np.random.default_rng(7)
     high = np.nonzero((lay.recv_pos >= first_high).any(axis=1))[0]
-    must = [int(lay.recv_token[first_high]), int(lay.recv_token[R - 1]), 0, T - 1]
+    owner = lay.recv_token[first_high:]
+    must = [int(owner[owner >= 0][0]), int(lay.recv_token[lay.recv_pos.max()]), 0, T - 1]
     pick = rng.choice(high, min(512, len(high)), replace=False)
     S = np.unique(np.concatenate([must, pick, rng.choice(T, 64, replace=False)])).astype(np.int64)
     say(f"{len(high)} tokens own rows past 4 GiB; {len(S)} tokens sampled")
     pos = lay.recv_pos[S]                   # [n, K] rows in the full problem
-    sub = O.layout(idx_np[S], E, P)         # the sampled tokens alone
+    sub = O.layout(idx_np[S], E, P, pad_multiple=pad)   # the sampled tokens alone
     spos = sub.recv_pos.reshape(-1)         # their rows in the sub-problem, in (token, k) order
     n = len(S)
     x_s, g_s = host_rows(x, S), host_rows(g, S)
-    y_s = np.zeros((n * K, H), np.uint16)
+    y_s = np.zeros((len(sub.recv_token), H), np.uint16)
     y_s[spos] = host_rows(y, pos)
     w_s = w_np[S]
 
