@@ -72,7 +72,7 @@ WsLayout plan_workspace(int64_t T, int K, int E, int P, int layout_pairs, int pa
   w.recv_k = take((size_t)cap * 4);
   w.send_token = take((size_t)T * (K < P ? K : P) * 4);
   w.tok_mask = take((size_t)T * 8);
-  w.hist = take((size_t)(E + 1 + P) * nblk * 4);
+  w.hist = take((size_t)(E + 1 + P) * (nblk + 1) * 4);  // a row per tile, and the totals of a scanned one
   w.total = o;
   return w;
 }
@@ -294,7 +294,7 @@ int layout_call(moe_handle_s* h, const void* topk_idx, int itype, int64_t T, int
   plan.hist = sized.hist;
   int* hist = nullptr;
   if (static_hist) {
-    if ((size_t)(E + 1 + P) * (size_t)plan.nblk * sizeof(int) > kScratchBytes) return MOE_ERR_SCRATCH;
+    if ((size_t)(E + 1 + P) * (size_t)(plan.nblk + 1) * sizeof(int) > kScratchBytes) return MOE_ERR_SCRATCH;
     void* p = nullptr;
     if ((st = scratch_address(stream, &p)) != MOE_OK) return st;
     hist = static_cast<int*>(p);

@@ -39,7 +39,9 @@ struct LayoutArgs {
   int itype, T, K, E, P, epr, nblk, tile;
   int pad;                // expert segments padded to a multiple of this
   int R;                  // receive rows (recv_capacity)
-  int* hist;              // [nblk][E+1+P]: per tile, bucket counts then partition token counts
+  int* hist;              // [nblk+1][E+1+P]: per tile, bucket counts then partition token counts
+  int scanned;            // hist rewritten by layout_scan_kernel: row j the counts of the tiles
+                          // before j, row nblk the column totals
   unsigned long long* tok_mask;  // [T] partitions each token is sent to
   int* num_tokens_per_expert;
   int* num_tokens_per_rank;

@@ -29,6 +29,11 @@
 //          layout_rank_kernel for larger tiles, which stages the ids in LDS
 //          and carries per-(wave, expert) cursors across rounds.
 //
+// Beyond 128 tiles a third launch sits between the two: layout_scan_kernel
+// rewrites the histogram once into per-tile column prefixes and a row of
+// totals, which each rank workgroup reads instead of summing every tile (that
+// sum would make the layout quadratic in the tile count).
+//
 // Ids outside [0,E) go to an extra bucket E, sorted after every expert, so
 // that every position stays inside [0, T*K) even for bad input; the rank
 // kernel raises MOE_STATUS_BAD_EXPERT for them.
@@ -42,6 +47,11 @@ namespace {
 constexpr int kLT = kLayoutThreads;  // threads per layout workgroup
 constexpr int kLW = kLT / kWave;     // waves per layout workgroup
 constexpr int kColRegs = 64;         // histogram tiles a scan thread loads at once
+// Above this many tiles the histogram's columns are scanned once, by
+// layout_scan_kernel, instead of by every rank workgroup (whose column sums
+// over all tiles would make the layout quadratic in the tile count).
+constexpr int kScanTiles = 128;
+constexpr int kScanBatch = 16;       // tiles a column-scan lane loads at once
 constexpr int kIdRegs = 2;           // tile ids a thread loads before the scan
 // token slots of a tile of at most 64 tokens: ballots per wave, and at most
 // this many rounds of the block over the tile's [tokens][P] items
@@ -186,13 +196,22 @@ __device__ __forceinline__ void all_column_sums(const int* __restrict__ h, int N
 // Each thread sums a range of tiles of one column with all its loads in
 // flight (clamped, unconditional loads); a workgroup scan over the column
 // totals follows.  part: LDS [2][parts][NR].  Ends with a barrier.
+// A scanned histogram (scanned != 0, parts == 1) already holds each column's
+// count in the tiles before b (row b) and its total (row nblk): two loads.
 __device__ void scan_histogram(const int* __restrict__ h, int NR, int nblk, int b, int npad, int pad,
-                               int* col_b, int* col_0, int* col_n, int* part, int* wsum) {
+                               int parts, int scanned, int* col_b, int* col_0, int* col_n, int* part,
+                               int* wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
-  const int parts = max(1, min(nblk, kLT / NR));  // threads per column
-  all_column_sums(h, NR, nblk, b, parts, part);
+  if (scanned) {
+    for (int r = tid; r < NR; r += kLT) {
+      part[r] = h[(size_t)nblk * NR + r];
+      part[NR + r] = h[(size_t)b * NR + r];
+    }
+  } else {
+    all_column_sums(h, NR, nblk, b, parts, part);
+  }
   __syncthreads();
   int carry = 0;
   for (int c0 = 0; c0 < NR; c0 += kLT) {  // uniform
@@ -270,11 +289,59 @@ __device__ __forceinline__ void write_slots(const LayoutArgs& a, const unsigned 
   }
 }
 
+// ---- column scan of a histogram of many tiles --------------------------------
+//
+// One workgroup per 64 histogram columns, lane = column; its eight waves
+// split the tiles into eight contiguous ranges.  Each wave sums its range,
+// the waves' sums are scanned through LDS, and each wave walks its range
+// again writing, in place, every tile's exclusive prefix (the column's count
+// in the tiles before it); row nblk gets the column totals.  Each histogram
+// entry is read and written by one thread only.  Linear in the tile count;
+// the loads of a lane are batched, clamped and unconditional.
+__global__ __launch_bounds__(kLT) void layout_scan_kernel(LayoutArgs a) {
+  __shared__ int wpart[kLW][kWave];
+  const int NR = a.E + 1 + a.P;
+  const int lane = lane_id();
+  const int w = (int)(threadIdx.x / kWave);
+  const int c = blockIdx.x * kWave + lane;
+  const int cc = min(c, NR - 1);  // clamped column for the loads
+  const int nb = a.nblk;
+  const int ch = (nb + kLW - 1) / kLW;
+  const int j0 = min(nb, w * ch), j1 = min(nb, j0 + ch);
+  int* h = a.hist;
+  int sum = 0;
+  for (int j = j0; j < j1; j += kScanBatch) {
+    int v[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) v[u] = h[(size_t)min(j + u, j1 - 1) * NR + cc];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) sum += (j + u < j1) ? v[u] : 0;
+  }
+  wpart[w][lane] = sum;
+  __syncthreads();
+  int run = 0;
+#pragma unroll
+  for (int q = 0; q < kLW; ++q) run += (q < w) ? wpart[q][lane] : 0;
+  for (int j = j0; j < j1; j += kScanBatch) {
+    int v[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) v[u] = h[(size_t)min(j + u, j1 - 1) * NR + cc];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      if (c < NR && j + u < j1) {
+        h[(size_t)(j + u) * NR + c] = run;
+        run += v[u];
+      }
+    }
+  }
+  if (w == kLW - 1 && c < NR) h[(size_t)nb * NR + c] = run;  // the last range ends at the total
+}
+
 __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   extern __shared__ __align__(8) unsigned char smem[];
   const int E1 = a.E + 1;
   const int NR = E1 + a.P;                   // histogram columns
-  const int parts = max(1, min(a.nblk, kLT / NR));
+  const int parts = a.scanned ? 1 : max(1, min(a.nblk, kLT / NR));  // threads per column of the scan
   unsigned long long* colm = reinterpret_cast<unsigned long long*>(smem);  // [P] tokens of the tile in partition r
   int* base = reinterpret_cast<int*>(colm + a.P);  // [NR]   this tile's start of each column
   int* off = base + NR;                      // [NR+1] start of each column, tile 0
@@ -317,7 +384,7 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
   for (int r = tid; r < a.P; r += kLT) carry[r] = 0;
 
   // 1. global offsets and this tile's starts (the scan ends with a barrier)
-  scan_histogram(a.hist, NR, a.nblk, b, a.E, a.pad, base, off, coln, part, wsum);
+  scan_histogram(a.hist, NR, a.nblk, b, a.E, a.pad, parts, a.scanned, base, off, coln, part, wsum);
 #pragma unroll
   for (int u = 0; u < kIdRegs; ++u) {
     const int i = tid + u * kLT;
@@ -687,12 +754,19 @@ bool layout_rank_wave_fits(int K, int E, int P, int tile) {
   return (int64_t)tile * K <= kLT && E + 1 + P <= kLT;
 }
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {
+hipError_t launch_layout(const LayoutArgs& a0, hipStream_t s) {
+  LayoutArgs a = a0;
+  a.scanned = a.nblk > kScanTiles ? 1 : 0;
   hipLaunchKernelGGL(layout_count_kernel, dim3(a.nblk), dim3(kLT), layout_count_lds(a.E, a.P, a.tile),
                      s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (layout_rank_wave_fits(a.K, a.E, a.P, a.tile))
+  if (a.scanned) {
+    const int NR = a.E + 1 + a.P;
+    hipLaunchKernelGGL(layout_scan_kernel, dim3((NR + kWave - 1) / kWave), dim3(kLT), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (!a.scanned && layout_rank_wave_fits(a.K, a.E, a.P, a.tile))
     hipLaunchKernelGGL(layout_rank_wave_kernel, dim3(a.nblk), dim3(kLT), layout_rank_wave_lds(a.E, a.P, a.tile),
                        s, a);
   else

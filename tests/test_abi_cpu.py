@@ -90,7 +90,7 @@ def test_noalloc_layout_host_checks(L):
         n = ctypes.c_size_t()
         T, K, E, P = 4096, 8, 128, 8
         assert L.moe_workspace_size(T, K, E, P, ctypes.byref(n)) == 0
-        hist = (E + 1 + P) * 64 * 4            # 64 tiles of 512 pairs
+        hist = (E + 1 + P) * 65 * 4            # 64 tiles of 512 pairs, and a row of totals
         f = L.moe_layout_noalloc
         assert f(None, FAKE, 0, T, K, E, P, FAKE, n.value, None) == C["MOE_ERR_INVALID_ARG"]
         assert f(h, FAKE, 0, T, K, 130, P, FAKE, n.value, None) == C["MOE_ERR_SHAPE"]

@@ -433,6 +433,38 @@ def test_long_context_token_count(absorbed):
     check_layout(h, O.layout(inp.topk_idx, cfg.E, cfg.P))
 
 
+SCANNED = [  # (T, K, E, P, id dtype, pad): more than 128 layout tiles, so the histogram is column-scanned
+    (262144 + 2049, 8, 128, 8, np.int32, 1),     # 130 tiles of 2048 tokens
+    ((1 << 20) + 7, 8, 256, 64, np.int32, 1),    # 513 tiles, the DeepSeek-V3 expert and partition counts
+    ((1 << 20) + 7, 8, 256, 64, np.int64, 1),
+    (300001, 8, 128, 8, np.int32, 16),           # padded segments
+    (1 << 21, 1, 1024, 64, np.int32, 1),         # about 690 tiles x 1089 columns: 18 scan workgroups
+]
+
+
+@pytest.mark.parametrize("T,K,E,P,dt,pad", SCANNED)
+def test_layout_scanned_histogram(T, K, E, P, dt, pad):
+    """Layouts of more than 128 tiles, whose histogram columns are scanned once
+    by their own kernel, against the oracle, bit for bit."""
+    say(f"scanned layout T={T} K={K} E={E} P={P} {np.dtype(dt).name} pad={pad}")
+    rng = np.random.default_rng(T + K + E + P)
+    idx = rng.integers(0, E, size=(T, K)).astype(dt)   # duplicate ids allowed, ordered by k
+    h = M.moe_layout(torch.from_numpy(idx).to(DEV), E, P, handle=M.Handle(pad_multiple=pad))
+    assert h.check() == 0
+    check_layout(h, O.layout(idx, E, P, pad_multiple=pad))
+
+
+def test_layer_scanned_histogram():
+    """A whole layer (every call) on a layout of 147 tiles."""
+    cfg = W.get_config("qwen3_30b_a3b").with_(T=300001, H=64)
+    say(f"layer on a scanned layout T={cfg.T} H={cfg.H}")
+    inp = W.layer_inputs(cfg, seed=52)
+    h, res = run_layer(cfg, inp)
+    lay, ref = oracle_layer(cfg, inp)
+    check_layout(h, lay)
+    compare_layer(cfg, res, ref)
+
+
 def test_unscaled_dispatch_with_scores_and_both_backward_modes():
     cfg = W.get_config("qwen3_30b_a3b", T=300)
     inp = W.layer_inputs(cfg, seed=4)
