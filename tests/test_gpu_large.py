@@ -187,3 +187,56 @@ def test_staged_rows_past_4_gib(absorbed):
     assert np.array_equal(host_rows(partial, full_send), r_part[sub_send]), "partials"
     r_out = O.combine_partitions(sub, r_part, DT)
     assert np.array_equal(host_rows(out, S), r_out), "merged rows"
+
+
+def test_layout_properties_at_half_a_billion_pairs():
+    """A layout of 2^29 - 24 pairs (T = 2^26 - 3, K = 8, E = 128, P = 8: 32768
+    tiles, so the histogram is column-scanned), checked on the device through
+    properties that define it at any size: the counts and offsets; recv_pos a
+    bijection onto [0, R) whose inverse is (recv_token, recv_k); experts in
+    ascending order and, inside an expert, pairs in (t, k) order; the send
+    schedule (is_token_in_rank, num_tokens_per_rank, send_offset, token_slot
+    as each token's rank in its partition's list, send_token its inverse).
+    Ids are drawn on the device by torch's seeded generator."""
+    T, K, E, P = (1 << 26) - 3, 8, 128, 8
+    R, epr = T * K, E // P
+    say(f"layout properties T={T} K={K} E={E} P={P}: {R} pairs")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(71)
+    idx = torch.randint(0, E, (T, K), generator=gen, device=DEV, dtype=torch.int32)
+    h = M.moe_layout(idx, E, P)
+    torch.cuda.synchronize()
+    assert h.check() == 0
+    flat = idx.reshape(-1)
+    cnt = torch.bincount(flat, minlength=E)
+    assert torch.equal(h.field("num_tokens_per_expert").long(), cnt)
+    eo = h.field("expert_offset").long()
+    assert eo[0].item() == 0 and torch.equal(eo[1:], torch.cumsum(cnt, 0))
+    inv = h.field("recv_token").long() * K + h.field("recv_k").long()      # pair at each receive row
+    assert int(inv.min()) >= 0 and int(inv.max()) < R
+    rows = torch.arange(R, device=DEV)
+    assert torch.equal(h.field("recv_pos").reshape(-1).long()[inv], rows)  # bijection, inverse consistent
+    del rows
+    e_at = flat[inv]                                                       # expert of each receive row
+    assert bool((e_at[1:] >= e_at[:-1]).all())                             # experts ascending
+    same = e_at[1:] == e_at[:-1]
+    assert bool((inv[1:] > inv[:-1])[same].all())                          # (t, k) order inside an expert
+    del e_at, same, inv
+    part = (idx // epr).long()
+    is_in = torch.zeros((T, P), dtype=torch.bool, device=DEV)
+    is_in.scatter_(1, part, True)
+    del part
+    assert torch.equal(h.field("is_token_in_rank").bool(), is_in)
+    ntr = is_in.sum(0)
+    assert torch.equal(h.field("num_tokens_per_rank").long(), ntr)
+    so = h.field("send_offset").long()
+    assert so[0].item() == 0 and torch.equal(so[1:], torch.cumsum(ntr, 0))
+    slot = torch.where(is_in, torch.cumsum(is_in, 0, dtype=torch.int32) - 1, torch.full_like(is_in, -1, dtype=torch.int32))
+    ts = h.field("token_slot")
+    assert torch.equal(ts, slot)
+    del slot, is_in
+    n_send = int(so[-1])
+    st = h.field("send_token")[:n_send].long()
+    q = torch.arange(n_send, device=DEV)
+    r = torch.searchsorted(so[1:], q, right=True)                          # partition of each send row
+    assert torch.equal(ts[st, r].long(), q - so[r])
