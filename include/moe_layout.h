@@ -189,9 +189,10 @@ int moe_layout(moe_handle_t h, const void* topk_idx, int itype, int64_t T, int K
  * has to hold the handle's arrays (moe_workspace_size() bytes always
  * suffice; the histogram section at their end is not touched).  The call
  * itself allocates nothing: no hipMalloc, hipFree or allocating library
- * routine.  Limit: the histogram, (E+1+P) * tiles * 4 bytes (tiles = about
- * T*K/512, at most a few hundred), must fit in 2 MiB; a larger shape is
- * refused on the host with MOE_ERR_SCRATCH, before any launch.  Every call
+ * routine.  Limit: the histogram, (E+1+P) * (tiles+1) * 4 bytes, must fit
+ * in 2 MiB (tiles: T*K/512, at most 128 until a tile reaches its cap of
+ * 2048 tokens at K = 8, then T/2048); a larger shape is refused on the host
+ * with MOE_ERR_SCRATCH, before any launch.  Every call
  * on one GPU shares that GPU's array: layouts that overlap in time on one
  * GPU (two streams, or two host threads) race on it and must be ordered by
  * the caller; each call writes every histogram entry it reads, so nothing
