@@ -337,6 +337,8 @@ RAGGED = [  # name, overrides
     ("deepseek_v3", dict(T=19, H=8712)),    # 18 segments: more than one per dot wave
     ("qwen3_30b_a3b", dict(T=77, H=4096)),  # 8 segments: the LDS gather keeps 4 waves per workgroup
     ("deepseek_v3", dict(T=23, H=8192)),    # 16 segments
+    ("deepseek_v3", dict(T=29, H=32768)),   # 64 KiB rows: 64 segments, four per dot wave
+    ("tiny", dict(T=33, H=16388)),          # f32 rows of 65552 bytes: 64 segments and a ragged tail
 ]
 
 
