@@ -29,7 +29,8 @@
 //          layout_rank_kernel for larger tiles, which stages the ids in LDS
 //          and carries per-(wave, expert) cursors across rounds.
 //
-// Beyond 128 tiles a third launch sits between the two: layout_scan_kernel
+// Beyond 128 tiles (and about 24K tiles x columns) a third launch sits
+// between the two: layout_scan_kernel
 // rewrites the histogram once into per-tile column prefixes and a row of
 // totals, which each rank workgroup reads instead of summing every tile (that
 // sum would make the layout quadratic in the tile count).
@@ -47,10 +48,14 @@ namespace {
 constexpr int kLT = kLayoutThreads;  // threads per layout workgroup
 constexpr int kLW = kLT / kWave;     // waves per layout workgroup
 constexpr int kColRegs = 64;         // histogram tiles a scan thread loads at once
-// Above this many tiles the histogram's columns are scanned once, by
-// layout_scan_kernel, instead of by every rank workgroup (whose column sums
-// over all tiles would make the layout quadratic in the tile count).
+// Above this many tiles, and tiles x columns, the histogram's columns are
+// scanned once, by layout_scan_kernel, instead of by every rank workgroup
+// (whose column sums over all tiles would make the layout quadratic in the
+// tile count).  Measured per layout against the unscanned form: at E = 128,
+// P = 8 (137 columns) 84.6 vs 81.9 us at 130 tiles, level at 196, 178 vs 184
+// at 293; at E = 256, P = 64 (321 columns) 204.4 vs 207.2 at 130 tiles.
 constexpr int kScanTiles = 128;
+constexpr int64_t kScanWork = 24576;  // tiles x columns
 constexpr int kScanBatch = 16;       // tiles a column-scan lane loads at once
 constexpr int kIdRegs = 2;           // tile ids a thread loads before the scan
 // token slots of a tile of at most 64 tokens: ballots per wave, and at most
@@ -756,7 +761,7 @@ bool layout_rank_wave_fits(int K, int E, int P, int tile) {
 
 hipError_t launch_layout(const LayoutArgs& a0, hipStream_t s) {
   LayoutArgs a = a0;
-  a.scanned = a.nblk > kScanTiles ? 1 : 0;
+  a.scanned = (a.nblk > kScanTiles && (int64_t)a.nblk * (a.E + 1 + a.P) > kScanWork) ? 1 : 0;
   hipLaunchKernelGGL(layout_count_kernel, dim3(a.nblk), dim3(kLT), layout_count_lds(a.E, a.P, a.tile),
                      s, a);
   hipError_t e = hipGetLastError();

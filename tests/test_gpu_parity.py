@@ -435,19 +435,22 @@ def test_long_context_token_count(absorbed):
     check_layout(h, O.layout(inp.topk_idx, cfg.E, cfg.P))
 
 
-SCANNED = [  # (T, K, E, P, id dtype, pad): more than 128 layout tiles, so the histogram is column-scanned
-    (262144 + 2049, 8, 128, 8, np.int32, 1),     # 130 tiles of 2048 tokens
+SCANNED = [  # (T, K, E, P, id dtype, pad): over 128 tiles and 24576 tiles x columns: the histogram is column-scanned
+    (400001, 8, 128, 8, np.int32, 1),            # 196 tiles of 2048 tokens x 137 columns
+    (262144 + 2049, 8, 256, 64, np.int32, 1),    # 130 tiles x 321 columns
     ((1 << 20) + 7, 8, 256, 64, np.int32, 1),    # 513 tiles, the DeepSeek-V3 expert and partition counts
     ((1 << 20) + 7, 8, 256, 64, np.int64, 1),
-    (300001, 8, 128, 8, np.int32, 16),           # padded segments
+    (400001, 8, 128, 8, np.int32, 16),           # padded segments
     (1 << 21, 1, 1024, 64, np.int32, 1),         # about 690 tiles x 1089 columns: 18 scan workgroups
+    (262144 + 2049, 8, 128, 8, np.int32, 1),     # 130 tiles x 137 columns: below the scan, the rank kernels sum
 ]
 
 
 @pytest.mark.parametrize("T,K,E,P,dt,pad", SCANNED)
 def test_layout_scanned_histogram(T, K, E, P, dt, pad):
     """Layouts of more than 128 tiles, whose histogram columns are scanned once
-    by their own kernel, against the oracle, bit for bit."""
+    by their own kernel (and one just below that work), against the oracle,
+    bit for bit."""
     say(f"scanned layout T={T} K={K} E={E} P={P} {np.dtype(dt).name} pad={pad}")
     rng = np.random.default_rng(T + K + E + P)
     idx = rng.integers(0, E, size=(T, K)).astype(dt)   # duplicate ids allowed, ordered by k
@@ -457,8 +460,8 @@ def test_layout_scanned_histogram(T, K, E, P, dt, pad):
 
 
 def test_layer_scanned_histogram():
-    """A whole layer (every call) on a layout of 147 tiles."""
-    cfg = W.get_config("qwen3_30b_a3b").with_(T=300001, H=64)
+    """A whole layer (every call) on a column-scanned layout of 196 tiles."""
+    cfg = W.get_config("qwen3_30b_a3b").with_(T=400001, H=64)
     say(f"layer on a scanned layout T={cfg.T} H={cfg.H}")
     inp = W.layer_inputs(cfg, seed=52)
     h, res = run_layer(cfg, inp)
