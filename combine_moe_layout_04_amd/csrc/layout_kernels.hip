@@ -29,11 +29,11 @@
 //          layout_rank_kernel for larger tiles, which stages the ids in LDS
 //          and carries per-(wave, expert) cursors across rounds.
 //
-// Beyond 128 tiles (and about 24K tiles x columns) a third launch sits
-// between the two: layout_scan_kernel
-// rewrites the histogram once into per-tile column prefixes and a row of
-// totals, which each rank workgroup reads instead of summing every tile (that
-// sum would make the layout quadratic in the tile count).
+// Beyond 128 tiles (and 24576 tiles x columns) a third launch sits between
+// the two: layout_scan_kernel rewrites the histogram once into per-tile
+// column prefixes and a row of totals, which each rank workgroup reads
+// instead of summing every tile (that sum would make the layout quadratic in
+// the tile count).
 //
 // Ids outside [0,E) go to an extra bucket E, sorted after every expert, so
 // that every position stays inside [0, T*K) even for bad input; the rank
