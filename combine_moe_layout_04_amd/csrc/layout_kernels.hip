@@ -29,6 +29,9 @@
 //          layout_rank_kernel for larger tiles, which stages the ids in LDS
 //          and carries per-(wave, expert) cursors across rounds.
 //
+// A layout of one tile (at most 512 pairs) is one launch: the wave form of
+// the rank kernel does the count itself.
+//
 // Beyond 128 tiles (and 24576 tiles x columns) a third launch sits between
 // the two: layout_scan_kernel rewrites the histogram once into per-tile
 // column prefixes and a row of totals, which each rank workgroup reads
@@ -563,6 +566,14 @@ __global__ __launch_bounds__(kLT) void layout_rank_kernel(LayoutArgs a) {
 // ballots) is done before or beside the scan, and the scan's last step also
 // turns the wave counts into each (wave, bucket)'s first receive row.
 
+// kOne: the whole layout is this one tile (T*K <= 512 pairs, one launch
+// instead of two).  The tile's counts and token masks are then made here
+// instead of read from the count kernel's global arrays: each token's thread
+// builds its mask from its K ids, each wave counts its tokens per partition
+// by ballots, and the bucket totals are the waves' bucket counts.  This
+// kernel also writes the count kernel's outputs: tok_mask, is_token_in_rank
+// and the cleared status.
+template <bool kOne>
 __global__ __launch_bounds__(kLT) void layout_rank_wave_kernel(LayoutArgs a) {
   extern __shared__ __align__(8) unsigned char smem[];
   const int E1 = a.E + 1;
@@ -590,12 +601,30 @@ __global__ __launch_bounds__(kLT) void layout_rank_wave_kernel(LayoutArgs a) {
   // 0. this thread's pair and token mask: their round trips overlap the
   //    histogram's.  Threads without a pair take an id no pair has.
   const int e = tid < np ? load_expert(a.idx, a.itype, p0 + tid, a.E) : a.E + 1;
-  const unsigned long long mk = tid < nt ? a.tok_mask[t0 + tid] : 0ull;
+  const unsigned long long mk = (!kOne && tid < nt) ? a.tok_mask[t0 + tid] : 0ull;
   int* mycnt = cnt + wv * E1;
   for (int j = lane; j < E1; j += kWave) mycnt[j] = 0;
-
-  // 1. column sums of the histogram, all of a thread's loads in flight
-  all_column_sums(a.hist, NR, a.nblk, b, parts, part);
+  if constexpr (kOne) {
+    // The status word is cleared by an exchange whose result thread 0 keeps:
+    // it has completed before barrier (1), so before any later OR into it.
+    if (tid == 0) wsum[0] = atomicExch(a.status, 0);
+    unsigned long long m = 0ull;
+    if (tid < nt) {
+      for (int k = 0; k < a.K; ++k) {
+        const int ek = load_expert(a.idx, a.itype, (int64_t)tid * a.K + k, a.E);
+        if (ek < a.E) m |= 1ull << (ek / a.epr);
+      }
+      tm[tid] = m;
+    }
+    int* wrc = part;  // [kLW][P] this wave's tokens per partition
+    for (int r = 0; r < a.P; ++r) {  // uniform
+      const int c = __popcll(__ballot((int)((m >> r) & 1ull)));
+      if (lane == 0) wrc[wv * a.P + r] = c;
+    }
+  } else {
+    // 1. column sums of the histogram, all of a thread's loads in flight
+    all_column_sums(a.hist, NR, a.nblk, b, parts, part);
+  }
 
   // 2. rank among the equal ids of this wave (wave64 ballots over the id
   //    bits), and the wave's count of each bucket, written by the highest
@@ -610,7 +639,7 @@ __global__ __launch_bounds__(kLT) void layout_rank_wave_kernel(LayoutArgs a) {
   const int rank = __popcll(same & lanes_below(lane));
   __builtin_amdgcn_wave_barrier();  // the wave's row is cleared before its counts land
   if (tid < np && (same >> lane) == 1ull) mycnt[e] = __popcll(same);
-  if (tid < nt) tm[tid] = mk;
+  if (!kOne && tid < nt) tm[tid] = mk;
   __syncthreads();  // (1)
 
   // 3. the scan's first half: each column's total, its count in the tiles
@@ -619,9 +648,19 @@ __global__ __launch_bounds__(kLT) void layout_rank_wave_kernel(LayoutArgs a) {
   //    partition) over the tile's token masks, spread over the waves.
   int tot = 0, pre = 0;
   if (tid < NR) {
-    for (int q = 0; q < parts; ++q) {
-      tot += part[q * NR + tid];
-      pre += part[(parts + q) * NR + tid];
+    if constexpr (kOne) {  // one tile: its own counts are the totals, nothing comes before it
+      if (tid < E1) {
+#pragma unroll
+        for (int w = 0; w < kLW; ++w) tot += cnt[w * E1 + tid];
+      } else {
+#pragma unroll
+        for (int w = 0; w < kLW; ++w) tot += part[w * a.P + tid - E1];
+      }
+    } else {
+      for (int q = 0; q < parts; ++q) {
+        tot += part[q * NR + tid];
+        pre += part[(parts + q) * NR + tid];
+      }
     }
   }
   const int seg = (tid < a.E) ? (tot + a.pad - 1) / a.pad * a.pad : tot;  // rows the column takes
@@ -732,6 +771,15 @@ __global__ __launch_bounds__(kLT) void layout_rank_wave_kernel(LayoutArgs a) {
     for (int r = tid; r <= a.P; r += kLT) a.send_offset[r] = off[E1 + r] - total;
     if (tid == 0 && off[a.E + 1] != off[a.E]) atomicOr(a.status, MOE_STATUS_BAD_EXPERT);
   }
+
+  // 9. one tile: the count kernel's per-token outputs
+  if constexpr (kOne) {
+    for (int tt = tid; tt < nt; tt += kLT) a.tok_mask[tt] = tm[tt];
+    for (int i = tid; i < nt * a.P; i += kLT) {
+      const int tt = i / a.P;
+      a.is_token_in_rank[i] = (uint8_t)((tm[tt] >> (i - tt * a.P)) & 1ull);
+    }
+  }
 }
 
 }  // namespace
@@ -762,6 +810,11 @@ bool layout_rank_wave_fits(int K, int E, int P, int tile) {
 hipError_t launch_layout(const LayoutArgs& a0, hipStream_t s) {
   LayoutArgs a = a0;
   a.scanned = (a.nblk > kScanTiles && (int64_t)a.nblk * (a.E + 1 + a.P) > kScanWork) ? 1 : 0;
+  if (a.nblk == 1 && layout_rank_wave_fits(a.K, a.E, a.P, a.tile)) {  // one tile: one launch
+    hipLaunchKernelGGL(layout_rank_wave_kernel<true>, dim3(1), dim3(kLT), layout_rank_wave_lds(a.E, a.P, a.tile),
+                       s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(layout_count_kernel, dim3(a.nblk), dim3(kLT), layout_count_lds(a.E, a.P, a.tile),
                      s, a);
   hipError_t e = hipGetLastError();
@@ -772,8 +825,8 @@ hipError_t launch_layout(const LayoutArgs& a0, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (!a.scanned && layout_rank_wave_fits(a.K, a.E, a.P, a.tile))
-    hipLaunchKernelGGL(layout_rank_wave_kernel, dim3(a.nblk), dim3(kLT), layout_rank_wave_lds(a.E, a.P, a.tile),
-                       s, a);
+    hipLaunchKernelGGL(layout_rank_wave_kernel<false>, dim3(a.nblk), dim3(kLT),
+                       layout_rank_wave_lds(a.E, a.P, a.tile), s, a);
   else
     hipLaunchKernelGGL(layout_rank_kernel, dim3(a.nblk), dim3(kLT),
                        layout_rank_lds(a.E, a.P, a.tile, a.K), s, a);
