@@ -82,14 +82,17 @@ def same(a, b):
                        b.view(torch.uint8) if b.dtype != torch.uint8 else b)
 
 
-@pytest.mark.parametrize("pad_multiple,staged,noalloc", [(1, False, False), (16, False, False), (1, True, False),
-                                                          (1, False, True), (16, True, True)])
-def test_step_replays_bitwise(pad_multiple, staged, noalloc):
+@pytest.mark.parametrize("pad_multiple,staged,noalloc,T", [(1, False, False, 1024), (16, False, False, 1024),
+                                                            (1, True, False, 1024), (1, False, True, 1024),
+                                                            (16, True, True, 1024), (1, False, False, 64),
+                                                            (1, False, True, 64), (16, True, False, 64)])
+def test_step_replays_bitwise(pad_multiple, staged, noalloc, T):
     """noalloc: the layout without a workspace histogram, the caller it is
     for; the layer run between replays also uses it, so the static scratch
-    holds another layer's histogram when each replay starts."""
-    cfg = W.get_config("qwen3_30b_a3b", T=1024)
-    say(f"graph pad={pad_multiple} staged={staged} noalloc={noalloc}")
+    holds another layer's histogram when each replay starts.  T = 64 (512
+    pairs, one tile) captures the one-launch layout."""
+    cfg = W.get_config("qwen3_30b_a3b", T=T)
+    say(f"graph pad={pad_multiple} staged={staged} noalloc={noalloc} T={T}")
     inp = W.layer_inputs(cfg, seed=11)
     h, out, step = make_step(cfg, inp, pad_multiple, staged, noalloc)
     # eager reference
